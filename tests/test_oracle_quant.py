@@ -1,0 +1,221 @@
+"""Pins of the oracle's amax, scale rule, casts, delayed-scaling history,
+blockwise and MX casts.
+
+What fixes each result:
+* amax: brute force over the decoded BF16 values (NaN > inf > finite order);
+* scale rule: closed forms (amax = fmax gives 1; amax = 2^k gives a power of two);
+* per-tensor cast: nearest-value property of every output code against the
+  FP32 product, exact scaling by powers of two, transposed copy = transpose;
+* delayed scaling (history window of past maxima, Colossal-AI story, section on
+  the two scaling schemes): hand-computed sequences over a 16-step window;
+* blockwise (guide, section "blockwise scaling"): uniform tiles reduce to
+  per-tensor, an outlier tile leaves the others untouched, brute force per tile;
+* MX (guide, section "MXFP8 scaling"): the E8M0 exponent against an exact
+  rational search over every positive finite BF16 amax.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+E4M3, E5M2 = 0, 1
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+def bf16_bits(vals):
+    """Exactly-representable float values -> BF16 bit patterns."""
+    f = np.asarray(vals, np.float32)
+    u = f.view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def rand_bf16(shape, seed, scale=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)   # truncation: any BF16 is fine
+
+
+def test_amax_brute_force(orc):
+    x = rand_bf16((37, 53), 1, 3.0)
+    vals = orc.bf16_to_f32(x).astype(np.float64)
+    assert orc.amax(x) == np.max(np.abs(vals))
+    x2 = x.copy()
+    x2[5, 7] = bf16_bits([-1000.0])[0]
+    assert orc.amax(x2) == 1000.0
+    x2[6, 8] = 0xFF80                                 # -inf
+    assert orc.amax(x2) == np.inf
+    x2[1, 1] = 0x7FC1                                 # NaN
+    assert np.isnan(orc.amax(x2))
+    assert orc.amax(bf16_bits([0.0, -0.0])) == 0.0
+    assert orc.amax(np.array([0x0001], np.uint16)) == 2.0 ** -133   # BF16 subnormal
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_scale_rule_closed_forms(orc, fmt):
+    fm = FMAX[fmt]
+    s, si = orc.scale_from_amax(fm, fmt)
+    assert s == 1.0 and si == 1.0
+    for k in range(-20, 21):
+        s, si = orc.scale_from_amax(2.0 ** k, fmt)
+        assert s == np.float32(fm / 2.0 ** k)            # exact: fmax * 2^-k
+        assert si == np.float32(2.0 ** k / fm)           # 1/s rounded once
+    for a in (0.0, np.inf, np.nan):
+        assert orc.scale_from_amax(a, fmt) == (1.0, 1.0)
+    s, si = orc.scale_from_amax(2.0 ** -133, fmt)          # quotient overflows FP32
+    assert s == np.finfo(np.float32).max
+    # FP32 division rounds to nearest: compare with exact rational quotient
+    for a in (3.0, 0.7, 1234.5, 1e-3):
+        a32 = float(np.float32(a))
+        s, _ = orc.scale_from_amax(a32, fmt)
+        q = Fraction(fm) / Fraction(a32)
+        lo = Fraction(float(np.nextafter(s, np.float32(0))))
+        hi = Fraction(float(np.nextafter(s, np.float32(np.inf))))
+        assert abs(Fraction(float(s)) - q) <= min(abs(lo - q), abs(hi - q))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_cast_is_nearest_code_of_fp32_product(orc, fmt):
+    x = rand_bf16((64, 96), 3, 2.0)
+    a = orc.amax(x)
+    s, si = orc.scale_from_amax(a, fmt)
+    q, qT, am = orc.quantize_tensor(x, fmt, s, transposed=True, want_amax=True)
+    assert am == a
+    assert np.array_equal(qT, q.T)
+    t = orc.decode_table(fmt)
+    p = (orc.bf16_to_f32(x) * np.float32(s)).astype(np.float64)   # one FP32 multiply
+    d = t[q]
+    # nothing representable is closer than the chosen code
+    fin = t[np.isfinite(t)]
+    dist = np.abs(d - p)
+    others = np.min(np.abs(fin[None, :] - p.reshape(-1, 1)), axis=1).reshape(p.shape)
+    assert np.all(dist <= others)
+    assert np.max(np.abs(d)) <= FMAX[fmt]
+    # current scaling maps amax onto the largest code (up to the FP32 rounding of s)
+    assert np.max(np.abs(d)) >= FMAX[fmt] * (1 - 2 ** -6)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_cast_power_of_two_scale_is_exact(orc, fmt):
+    t = orc.decode_table(fmt)
+    codes = np.array([c for c in range(256) if np.isfinite(t[c])], np.uint8)
+    v = t[codes]                                      # every FP8 value
+    for k in (-3, 0, 2):
+        x = bf16_bits((v * 2.0 ** -k).astype(np.float32)).reshape(1, -1)
+        q, _, _ = orc.quantize_tensor(x, fmt, np.float32(2.0 ** k))
+        assert np.array_equal(t[q[0]], v)
+
+
+def test_history_window_sequence(orc):
+    H = 16
+    hist = np.zeros(H, np.float32)
+    # decreasing maxima: the window max is the oldest entry still in the window
+    for t in range(40):
+        a = float(100 - t)
+        s, si = orc.amax_history_update(hist, t, a, E4M3)
+        want_max = 100.0 if t < H else float(100 - (t - H + 1))
+        assert s == np.float32(448.0 / want_max), t
+        assert si == np.float32(1.0 / np.float32(448.0 / want_max))
+    # a spike stays in the window for exactly H steps
+    hist = np.zeros(H, np.float32)
+    for t in range(50):
+        a = 1000.0 if t == 5 else 1.0
+        s, _ = orc.amax_history_update(hist, t, a, E5M2)
+        want = 1000.0 if 5 <= t < 5 + H else 1.0
+        assert s == np.float32(57344.0 / want), t
+    # slot = step % H; the first steps see zeros elsewhere
+    hist = np.zeros(H, np.float32)
+    orc.amax_history_update(hist, 0, 2.0, E4M3)
+    assert hist[0] == 2.0 and np.all(hist[1:] == 0)
+    orc.amax_history_update(hist, 17, 3.0, E4M3)
+    assert hist[1] == 3.0
+    # NaN in the window makes the scale fall back to 1 until it leaves
+    hist = np.zeros(H, np.float32)
+    for t in range(20):
+        s, _ = orc.amax_history_update(hist, t, np.nan if t == 2 else 4.0, E4M3)
+        assert s == (1.0 if 2 <= t < 2 + H else np.float32(448.0 / 4.0)), t
+
+
+def _per_tile_brute(orc, x, fmt, br, bc):
+    R, C = x.shape
+    q = np.empty_like(x, dtype=np.uint8)
+    si = np.empty((R // br, C // bc), np.float32)
+    for i in range(R // br):
+        for j in range(C // bc):
+            tile = x[i * br:(i + 1) * br, j * bc:(j + 1) * bc]
+            s, sinv = orc.scale_from_amax(orc.amax(tile), fmt)
+            si[i, j] = sinv
+            q[i * br:(i + 1) * br, j * bc:(j + 1) * bc] = orc.quantize_tensor(
+                np.ascontiguousarray(tile), fmt, s)[0]
+    return q, si
+
+
+@pytest.mark.parametrize("br", [1, 128])
+def test_blockwise_brute_force_and_reductions(orc, br):
+    x = rand_bf16((256, 384), 5, 1.0)
+    q, si = orc.quantize_block(x, E4M3, br, 128)
+    qb, sib = _per_tile_brute(orc, x, E4M3, br, 128)
+    assert np.array_equal(q, qb) and np.array_equal(si, sib)
+    # uniform tiles: plant the same maximum in every tile -> per-tensor result
+    xu = x.copy()
+    for i in range(256 // br):
+        for j in range(3):
+            xu[i * br, j * 128] = bf16_bits([64.0])[0]
+    xu = np.where(orc.bf16_to_f32(xu) > 64.0, bf16_bits([1.0])[0], xu).astype(np.uint16)
+    xu = np.where(orc.bf16_to_f32(xu) < -64.0, bf16_bits([-1.0])[0], xu).astype(np.uint16)
+    qu, siu = orc.quantize_block(xu, E4M3, br, 128)
+    s, sinv = orc.scale_from_amax(orc.amax(xu), E4M3)
+    qt, _, _ = orc.quantize_tensor(xu, E4M3, s)
+    assert np.array_equal(qu, qt) and np.all(siu == sinv)
+    # an outlier in one tile changes only that tile
+    xo = x.copy()
+    xo[0, 0] = bf16_bits([8192.0])[0]
+    qo, sio = orc.quantize_block(xo, E4M3, br, 128)
+    mask = np.ones_like(q, dtype=bool)
+    mask[0:br, 0:128] = False
+    assert np.array_equal(qo[mask], q[mask])
+    assert sio[0, 0] != si[0, 0] and np.array_equal(sio.reshape(-1)[1:], si.reshape(-1)[1:])
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_mx_exponent_every_bf16_amax(orc, fmt):
+    """Smallest integer e with a <= fmax * 2^e, by exact search, for all
+    32639 positive finite BF16 values."""
+    fm = Fraction(FMAX[fmt])
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    for a in vals:
+        e = orc.mx_exponent(float(a), fmt)
+        fa = Fraction(float(a))
+        # exact: e = ceil(log2(a / fmax)) by search from a floor estimate
+        g = math.floor(math.log2(float(a)) - math.log2(FMAX[fmt])) - 1
+        while fa > fm * Fraction(2) ** g:
+            g += 1
+        g = max(-127, min(127, g))
+        assert e == g, (float(a), e, g)
+        if g > -127:
+            scaled = fa / Fraction(2) ** e
+            assert fm / 2 < scaled <= fm                    # never saturates
+
+
+def test_mx_cast_blocks(orc):
+    x = rand_bf16((8, 128), 9, 1.0)
+    x[1, 0:32] = 0                                      # all-zero block
+    x[2, 32] = 0x7FC0                                   # NaN block
+    x[3, 64:96] = bf16_bits([2.0 ** -130] * 32)         # deep subnormal block
+    q, e = orc.quantize_mx(x, E4M3)
+    assert e[1, 0] == 127 and np.all(q[1, 0:32] == 0)
+    assert e[2, 1] == 0xFF and q[2, 32] == 0x7F
+    t = orc.decode_table(E4M3)
+    for r in range(8):
+        for b in range(4):
+            if e[r, b] == 0xFF:
+                continue
+            blk = orc.bf16_to_f32(x[r, b * 32:(b + 1) * 32]).astype(np.float64)
+            scale = 2.0 ** (int(e[r, b]) - 127)
+            d = t[q[r, b * 32:(b + 1) * 32]] * scale
+            # power-of-two scaling is exact, so only the FP8 rounding remains
+            assert np.all(np.abs(d - blk) <= np.abs(blk) * 2 ** -4 + scale * 2.0 ** -10)
+            if np.any(blk != 0):
+                assert np.max(np.abs(t[q[r, b * 32:(b + 1) * 32]])) >= 224.0 or e[r, b] == 0
