@@ -106,8 +106,11 @@ def test_saturation_and_specials(orc, fmt, fmax, maxc):
     big = [fmax * (1 + 2 ** -20), np.inf, 1e30, 3.0e38, fmax * 1.06, fmax * 1.5]
     assert list(orc.encode(np.array(big, np.float32), fmt)) == [maxc] * len(big)
     assert list(orc.encode(-np.array(big, np.float32), fmt)) == [0x80 | maxc] * len(big)
-    assert orc.encode([np.float32(np.nan)], fmt)[0] == 0x7F
-    assert orc.encode([-np.float32(np.nan)], fmt)[0] == 0xFF
+    # NaN (any sign or payload) -> the format's canonical NaN code
+    nan_code = 0xFF if fmt == E4M3 else 0xFE
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32).view(np.float32)
+    assert list(orc.encode(nans, fmt)) == [nan_code] * 4
+    assert np.isnan(orc.decode_table(fmt)[nan_code])
     assert orc.encode([np.float32(0.0)], fmt)[0] == 0x00
     assert orc.encode([np.float32(-0.0)], fmt)[0] == 0x80
     # FP32 subnormals and values below half the smallest FP8 subnormal -> signed zero
@@ -136,7 +139,7 @@ def _nearest_codec(fmt, orc):
                                                               codes[hi])))
         pick = np.where(a >= vals[top], top, pick)
         pick = np.where(np.signbit(f), pick | 0x80, pick)
-        pick = np.where(np.isnan(f), np.where(np.signbit(f), 0xFF, 0x7F), pick)
+        pick = np.where(np.isnan(f), 0xFF if fmt == E4M3 else 0xFE, pick)
         return pick.astype(np.uint8)
     return enc
 
