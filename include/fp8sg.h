@@ -1,0 +1,186 @@
+/*
+ * fp8sg.h -- C ABI of libfp8sg.so: FP8 quantisation under a scaling recipe and
+ * the scaled FP8 GEMMs of a linear layer, as HIP kernels for MI355X (gfx950).
+ *
+ * What the calls compute is stated by these pages (cited by title and section):
+ *   [guide]    "FP8 quantisation training practical guide" (scrxy.com): section
+ *              "format choice: E4M3 and E5M2"; section "three scaling
+ *              algorithms" (tensor-level, delayed with a buffer of past maxima,
+ *              just-in-time from the current batch's maximum); section
+ *              "blockwise scaling" (E4M3 only, 1x128 tiles for inputs and
+ *              gradients, 128x128 blocks for weights, one scale per block);
+ *              section "MXFP8 scaling" (1x32 blocks, E8M0 scales); section
+ *              "code changes" (the three GEMMs of a Transformer layer take
+ *              quantised inputs, outputs stay BF16).
+ *   [colossal] QbitAI story on Colossal-AI FP8 mixed-precision training:
+ *              paragraph on delayed vs real-time scaling.
+ *   [snippets] "fp8+bf8" search-result page: the forward-pass snippet (BF16
+ *              input, weights quantised to FP8, output back to BF16 after
+ *              accumulation; dgrad cast to BF16 after the FP8 backward GEMM).
+ *
+ * Conventions for every call
+ *   Memory      Every pointer argument except `stream` is device memory owned by
+ *               the caller.  The library allocates nothing and keeps no state
+ *               between calls.  Tensors are dense and row-major.
+ *   Stream      `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *               enqueue kernels and return; nothing synchronises.  Outputs are
+ *               valid once the stream has passed the call.
+ *   Formats     FP8 bytes follow the OCP 8-bit formats: E4M3 is E4M3FN (bias 7,
+ *               no infinity, max 448, NaN = S.1111.111); E5M2 has bias 15, max
+ *               57344, IEEE-style inf/NaN.  BF16 tensors are passed as 16-bit
+ *               words.  The cast is: one FP32 multiply x*scale, magnitudes above
+ *               the format's maximum (and +-inf) saturate to +-max, any NaN
+ *               becomes the canonical NaN code (0xFF for E4M3, 0xFE for E5M2,
+ *               the gfx950 converter's codes), the rest rounds to nearest even.
+ *   Scale rule  scale = fmax / amax in FP32 (fmax = 448 or 57344); 1 when amax
+ *               is 0, inf or NaN; FLT_MAX when the quotient overflows.
+ *               scale_inv = 1 / scale in FP32.  Quantise multiplies by scale,
+ *               dequantise multiplies by scale_inv.
+ *   amax        max |x| under the order NaN > inf > finite on magnitude bits, so
+ *               a NaN anywhere gives a NaN amax.  Always exactly a BF16 value.
+ *   Errors      Arguments are checked on the host before anything is enqueued;
+ *               a failing check returns its status and has no side effect.
+ *               FP8_ERR_HIP reports a launch failure.  NaN/inf data are not
+ *               errors; they follow the rules above.
+ *   Alignment   Data pointers must be 16-byte aligned (FP8_ERR_ALIGN).
+ *   Empty       A tensor with zero elements may be passed as NULL; required
+ *               pointers to non-empty tensors and to outputs such as amax may
+ *               not (FP8_ERR_NULL).
+ */
+#ifndef FP8SG_H
+#define FP8SG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format_t;
+
+typedef enum {
+  FP8_SCALE_TENSOR = 0,        /* scale_inv: float[1]                                */
+  FP8_SCALE_BLOCK_1x128 = 1,   /* scale_inv: float[rows][K/128]                      */
+  FP8_SCALE_BLOCK_128x128 = 2, /* scale_inv: float[rows/128][K/128]                  */
+  FP8_SCALE_MX_1x32 = 3        /* scale_inv: uint8 E8M0 [rows][K/32], byte = e + 127 */
+} fp8_scaling_t;
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FP8_ERR_SHAPE = 2,       /* negative size, or a size that breaks a block rule   */
+  FP8_ERR_ALIGN = 3,       /* pointer or row length not suitably aligned          */
+  FP8_ERR_UNSUPPORTED = 4, /* unknown enum value or unsupported combination       */
+  FP8_ERR_HIP = 5          /* the HIP runtime rejected a launch                   */
+} fp8_status_t;
+
+/* One quantised GEMM operand: `data` is FP8 [rows][K] row-major (K contiguous,
+ * K = the GEMM's contraction length), with its dequantisation scales. */
+typedef struct {
+  const uint8_t* data;
+  int32_t fmt;             /* fp8_format_t  */
+  int32_t scaling;         /* fp8_scaling_t */
+  const void* scale_inv;   /* layout per fp8_scaling_t above */
+} fp8_operand_t;
+
+/* amax of a BF16 tensor and, optionally, the scale pair it implies.
+ * [colossal] real-time scaling / [guide] just-in-time scaling: the scale comes
+ * from the maximum of the tensor being cast.
+ *   x_bf16     [rows][cols] BF16, 16-byte aligned (any rows, cols >= 0)
+ *   amax       out float[1]
+ *   scale, scale_inv   out float[1] each, nullable (scale rule above)
+ * Errors: NULL x/amax; negative sizes; misaligned x; fmt not E4M3/E5M2. */
+fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                      float* amax, float* scale, float* scale_inv, void* stream);
+
+/* Per-tensor cast q = cast(x * scale[0]).  [guide] code changes: the GEMM
+ * inputs are quantised; the transposed copy qT is the K-contiguous operand the
+ * weight-gradient GEMM reads.
+ *   x_bf16   [rows][cols] BF16;  cols % 16 == 0 (FP8_ERR_ALIGN)
+ *   scale    in float[1] (device)
+ *   q        out uint8 [rows][cols]
+ *   qT       out uint8 [cols][rows], nullable; needs rows % 16 == 0
+ *   amax_out out float[1], nullable: amax of x, fused into the same pass
+ *            (delayed scaling records it in its history; [colossal] delayed
+ *            scaling fuses the scale update with the GEMM pipeline)
+ * Errors: NULL x/scale/q; negative sizes; alignment; fmt. */
+fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                 const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                 void* stream);
+
+/* One delayed-scaling step.  [guide] delayed scaling keeps a buffer of the
+ * maxima of past steps; [colossal] delayed scaling takes the scale from a
+ * window of past values.
+ *   history  in/out float[history_len] (1..1024), ring buffer; zeros initially
+ *   step     >= 0: amax[0] is written to history[step % history_len]
+ *   amax     in float[1] (device), this step's amax
+ *   scale, scale_inv  out float[1]: the scale rule applied to max(history)
+ *            (NaN propagates), i.e. the pair step+1 uses.
+ * Order on one stream at step t: quantise with scale_t (fused amax) -> GEMMs
+ * reading scale_inv_t -> this call with step = t.
+ * Errors: NULL pointers; history_len out of range; step < 0; fmt. */
+fp8_status_t fp8_amax_history_update(float* history, int32_t history_len, int64_t step,
+                                     const float* amax, int32_t fmt, float* scale,
+                                     float* scale_inv, void* stream);
+
+/* Blockwise cast.  [guide] blockwise scaling: E4M3, inputs and gradients in
+ * 1x128 tiles, weights in 128x128 blocks, each block scaled on its own.
+ * Tiles run along the contiguous (contraction) dimension.
+ *   block_rows  1 or 128;  block_cols  128
+ *   x_bf16      [rows][cols] BF16, cols % 128 == 0, rows % block_rows == 0
+ *   q           out uint8 [rows][cols]
+ *   scale_inv   out float [rows/block_rows][cols/128]
+ * Both FP8 formats are accepted (the pages use E4M3).
+ * Errors: NULL; sizes; block shape; alignment; fmt. */
+fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                int32_t block_rows, int32_t block_cols, uint8_t* q,
+                                float* scale_inv, void* stream);
+
+/* MX cast.  [guide] MXFP8 scaling: uniform 1x32 blocks with E8M0 scales.
+ * Per block along the contiguous dimension: e = the smallest integer with
+ * amax <= fmax * 2^e (clamped to [-127, 127]), byte = e + 127; an all-zero
+ * block gets 127; a block with inf/NaN gets 0xFF and its elements are cast
+ * unscaled; q = cast(x * 2^-e).  Dequantisation multiplies by 2^e.
+ *   x_bf16     [rows][cols] BF16, cols % 32 == 0
+ *   q          out uint8 [rows][cols]
+ *   scale_e8m0 out uint8 [rows][cols/32]
+ * Errors: NULL; sizes; alignment; fmt. */
+fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                             uint8_t* q, uint8_t* scale_e8m0, void* stream);
+
+/* The three GEMMs of a linear layer ([guide] code changes; [snippets] forward
+ * and backward flow), FP32 accumulation on MFMA, BF16 output (round to nearest
+ * even).  Both operands are K-contiguous ("TN"), so one kernel serves all three:
+ *   fprop  y[M][N]  = sum_k x[M][K](m,k)   * w[N][K](n,k)      (contract K)
+ *   dgrad  dx[M][K] = sum_n dy[M][N](m,n)  * wT[K][N](k,n)     (contract N)
+ *   wgrad  dw[N][K] = sum_m dyT[N][M](n,m) * xT[K][M](k,m)     (contract M)
+ * Scaling of each output element c[i][j] over contraction index t:
+ *   tensor x tensor:  (sa[0] * sb[0]) * sum_t a(i,t) b(j,t)
+ *   block  x block :  sum_b sa(i,b) * sb(j,b) * sum_{t in block b} a(i,t) b(j,t)
+ *                     (each operand 1x128 or 128x128; 128-wide blocks along t)
+ *   MX     x MX    :  sum_t a(i,t) 2^ea(i,t/32) * b(j,t) 2^eb(j,t/32)
+ * Shape rules: sizes >= 0; contraction % 16 == 0 (FP8_ERR_ALIGN); block
+ * operands need contraction % 128 == 0 and, for 128x128, rows % 128 == 0; MX
+ * needs contraction % 32 == 0 (FP8_ERR_SHAPE).  Mixed families are
+ * FP8_ERR_UNSUPPORTED.  Output pointers must be 16-byte aligned.
+ * Errors: NULL operand/data/scale/output; shapes; alignment; enums. */
+fp8_status_t fp8_gemm_fprop(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,
+                            int64_t N, int64_t K, void* y_bf16, void* stream);
+fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, int64_t M,
+                            int64_t N, int64_t K, void* dx_bf16, void* stream);
+fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
+                            int64_t N, int64_t K, void* dw_bf16, void* stream);
+
+/* The cast's rounding step alone: q[i] = cast(x[i]) for FP32 inputs (no
+ * scaling).  Every quantise kernel above rounds through the same device
+ * routine; this entry point lets that routine be checked on any FP32 input.
+ *   x  in float[n];  q  out uint8[n].  Errors: NULL; n < 0; alignment; fmt. */
+fp8_status_t fp8_convert_f32(const float* x, int64_t n, int32_t fmt, uint8_t* q, void* stream);
+
+/* Text for a status code (static storage). */
+const char* fp8_status_string(fp8_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8SG_H */

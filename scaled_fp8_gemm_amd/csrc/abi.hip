@@ -1,0 +1,185 @@
+// abi.hip -- the extern "C" entry points of libfp8sg (declared and documented
+// in include/fp8sg.h).  Each call checks its arguments on the host, in the
+// order NULL -> enum -> shape -> alignment (a NULL data pointer is accepted
+// for an empty tensor, so the NULL check of data follows the shape check),
+// and only then enqueues kernels on the caller's stream.  Nothing here
+// allocates or synchronises.
+#include "fp8sg.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+using fp8sg::GemmProblem;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;           // rows / cols limit
+constexpr int64_t kMaxTileRows = (int64_t)65535 * 128;  // 2-D launch grid limit
+
+bool fmt_ok(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool dims_ok(int64_t r, int64_t c) { return r >= 0 && c >= 0 && r < kMaxDim && c < kMaxDim; }
+fp8_status_t hip(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+hipStream_t st(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A data pointer may be NULL only when the tensor it points to is empty.
+bool have(const void* p, int64_t elems) { return p != nullptr || elems == 0; }
+
+bool is_block(int32_t sc) { return sc == FP8_SCALE_BLOCK_1x128 || sc == FP8_SCALE_BLOCK_128x128; }
+
+// C[rows_a][rows_b] = A[rows_a][kc] . B[rows_b][kc]^T with the operands' scales.
+fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a,
+                  int64_t rows_b, int64_t kc, void* c, void* stream) {
+  if (!a || !b) return FP8_ERR_NULL;
+  if (!fmt_ok(a->fmt) || !fmt_ok(b->fmt)) return FP8_ERR_UNSUPPORTED;
+  if (a->scaling < FP8_SCALE_TENSOR || a->scaling > FP8_SCALE_MX_1x32 ||
+      b->scaling < FP8_SCALE_TENSOR || b->scaling > FP8_SCALE_MX_1x32)
+    return FP8_ERR_UNSUPPORTED;
+  int mode;
+  if (a->scaling == FP8_SCALE_TENSOR && b->scaling == FP8_SCALE_TENSOR)
+    mode = 0;
+  else if (is_block(a->scaling) && is_block(b->scaling))
+    mode = 1;
+  else if (a->scaling == FP8_SCALE_MX_1x32 && b->scaling == FP8_SCALE_MX_1x32)
+    mode = 2;
+  else
+    return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows_a, kc) || !dims_ok(rows_b, kc)) return FP8_ERR_SHAPE;
+  const int64_t nc = rows_a * rows_b;
+  if (!have(a->data, rows_a * kc) || !have(b->data, rows_b * kc) || !have(c, nc) ||
+      !have(a->scale_inv, nc) || !have(b->scale_inv, nc))
+    return FP8_ERR_NULL;
+  if (mode == 1) {
+    if (kc % 128) return FP8_ERR_SHAPE;
+    if (a->scaling == FP8_SCALE_BLOCK_128x128 && rows_a % 128) return FP8_ERR_SHAPE;
+    if (b->scaling == FP8_SCALE_BLOCK_128x128 && rows_b % 128) return FP8_ERR_SHAPE;
+  }
+  if (mode == 2 && kc % 32) return FP8_ERR_SHAPE;
+  if (kc % 16) return FP8_ERR_ALIGN;
+  if (!aligned(a->data, 16) || !aligned(b->data, 16) || !aligned(c, 16)) return FP8_ERR_ALIGN;
+  if (mode != 2 && (!aligned(a->scale_inv, 4) || !aligned(b->scale_inv, 4)))
+    return FP8_ERR_ALIGN;
+  GemmProblem p;
+  p.A = a->data;
+  p.B = b->data;
+  p.sa = a->scale_inv;
+  p.sb = b->scale_inv;
+  p.C = static_cast<uint16_t*>(c);
+  p.M = rows_a;
+  p.N = rows_b;
+  p.K = kc;
+  p.fa = a->fmt;
+  p.fb = b->fmt;
+  p.mode = mode;
+  p.bra = a->scaling == FP8_SCALE_BLOCK_128x128 ? 128 : 1;
+  p.brb = b->scaling == FP8_SCALE_BLOCK_128x128 ? 128 : 1;
+  return hip(fp8sg::launch_gemm(p, st(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt, float* amax,
+                      float* scale, float* scale_inv, void* stream) {
+  if (!amax) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols)) return FP8_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(amax, 4) || (scale && !aligned(scale, 4)) ||
+      (scale_inv && !aligned(scale_inv, 4)))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_amax(x_bf16, rows * cols, fmt, amax, scale, scale_inv, st(stream)));
+}
+
+fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                 const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                 void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols) || !have(q, rows * cols) || !have(scale, rows * cols))
+    return FP8_ERR_NULL;
+  if (qT && rows > kMaxTileRows) return FP8_ERR_SHAPE;
+  if (cols % 16) return FP8_ERR_ALIGN;
+  if (qT && rows % 16) return FP8_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||
+      !aligned(scale, 4) || (amax_out && !aligned(amax_out, 4)))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_tensor(x_bf16, rows, cols, fmt, scale, q, qT, amax_out,
+                                           st(stream)));
+}
+
+fp8_status_t fp8_amax_history_update(float* history, int32_t history_len, int64_t step,
+                                     const float* amax, int32_t fmt, float* scale,
+                                     float* scale_inv, void* stream) {
+  if (!history || !amax || !scale || !scale_inv) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (history_len < 1 || history_len > 1024 || step < 0) return FP8_ERR_SHAPE;
+  if (!aligned(history, 4) || !aligned(amax, 4) || !aligned(scale, 4) || !aligned(scale_inv, 4))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_history_update(history, history_len, step, amax, fmt, scale,
+                                          scale_inv, st(stream)));
+}
+
+fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                int32_t block_rows, int32_t block_cols, uint8_t* q,
+                                float* scale_inv, void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols) || !have(q, rows * cols) || !have(scale_inv, rows * cols))
+    return FP8_ERR_NULL;
+  if ((block_rows != 1 && block_rows != 128) || block_cols != 128) return FP8_ERR_UNSUPPORTED;
+  if (cols % 128 || rows % block_rows) return FP8_ERR_SHAPE;
+  if (block_rows == 128 && rows > kMaxTileRows) return FP8_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scale_inv, 4)) return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_block(x_bf16, rows, cols, fmt, block_rows, q, scale_inv,
+                                          st(stream)));
+}
+
+fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                             uint8_t* q, uint8_t* scale_e8m0, void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols) || cols % 32) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols) || !have(q, rows * cols) || !have(scale_e8m0, rows * cols))
+    return FP8_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_mx(x_bf16, rows, cols, fmt, q, scale_e8m0, st(stream)));
+}
+
+fp8_status_t fp8_gemm_fprop(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M, int64_t N,
+                            int64_t K, void* y_bf16, void* stream) {
+  return gemm(x, w, M, N, K, y_bf16, stream);
+}
+
+fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, int64_t M,
+                            int64_t N, int64_t K, void* dx_bf16, void* stream) {
+  return gemm(dy, wT, M, K, N, dx_bf16, stream);
+}
+
+fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
+                            int64_t N, int64_t K, void* dw_bf16, void* stream) {
+  return gemm(dyT, xT, N, K, M, dw_bf16, stream);
+}
+
+fp8_status_t fp8_convert_f32(const float* x, int64_t n, int32_t fmt, uint8_t* q, void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (n < 0) return FP8_ERR_SHAPE;
+  if (!have(x, n) || !have(q, n)) return FP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_convert(x, n, fmt, q, st(stream)));
+}
+
+const char* fp8_status_string(fp8_status_t status) {
+  switch (status) {
+    case FP8_OK: return "FP8_OK";
+    case FP8_ERR_NULL: return "FP8_ERR_NULL: a required pointer is NULL";
+    case FP8_ERR_SHAPE: return "FP8_ERR_SHAPE: size out of range or not a block multiple";
+    case FP8_ERR_ALIGN: return "FP8_ERR_ALIGN: pointer or row length not aligned";
+    case FP8_ERR_UNSUPPORTED: return "FP8_ERR_UNSUPPORTED: unknown enum or unsupported combination";
+    case FP8_ERR_HIP: return "FP8_ERR_HIP: kernel launch failed";
+  }
+  return "unknown fp8_status_t";
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// launch.h -- internal launchers of libfp8sg (host side).  Arguments have been
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8sg {
+
+int device_cu_count();
+
+hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
+                       float* scale_inv, hipStream_t s);
+hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
+                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                  hipStream_t s);
+hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
+                                 float* scale, float* scale_inv, hipStream_t s);
+hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,
+                                 uint8_t* q, float* scale_inv, hipStream_t s);
+hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                              uint8_t* e8m0, hipStream_t s);
+hipError_t launch_convert(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s);
+
+// C[M][N] (BF16) = A[M][K] . B[N][K]^T with the operands' scales.
+// mode: 0 tensor, 1 block (bra/brb = 1 or 128 rows per scale), 2 MX.
+struct GemmProblem {
+  const uint8_t* A;
+  const uint8_t* B;
+  const void* sa;
+  const void* sb;
+  uint16_t* C;
+  int64_t M, N, K;
+  int fa, fb;
+  int mode;
+  int bra, brb;
+};
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
+
+}  // namespace fp8sg

@@ -1,0 +1,404 @@
+// quant.hip -- amax, scale, per-tensor / blockwise / MX casts and the
+// delayed-scaling history update, as gfx950 kernels.
+//
+// What is computed follows the FP8 quantisation training guide (sections
+// "three scaling algorithms", "blockwise scaling", "MXFP8 scaling") and the
+// Colossal-AI FP8 story (paragraph on delayed vs real-time scaling); the exact
+// rules are restated in include/fp8sg.h.  All of these kernels are bound by
+// HBM bandwidth: every element is read once as BF16 (2 B) and written once per
+// FP8 copy (1 B); they use 16-byte vector loads, grid-stride loops sized to
+// the CU count, and reduce maxima as unsigned magnitude bits (exact, and
+// order-independent, so atomicMax gives the same result on every run).
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8sg {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
+}
+
+// amax over n BF16 values: nvec 16-byte vectors plus a tail of < 8 elements.
+__global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ x, int64_t nvec,
+                                                   const uint16_t* __restrict__ tail, int ntail,
+                                                   uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    uint4 v0 = ld_stream(&x[i]);
+    uint4 v1 = ld_stream(&x[i + stride]);
+    uint4 v2 = ld_stream(&x[i + 2 * stride]);
+    uint4 v3 = ld_stream(&x[i + 3 * stride]);
+    m = max(m, max(max(absmax8(v0), absmax8(v1)), max(absmax8(v2), absmax8(v3))));
+  }
+  for (; i < nvec; i += stride) m = max(m, absmax8(x[i]));
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7fffu));
+  m = block_max_u32<kThreads>(m, red);
+  if (threadIdx.x == 0) atomicMax(out, m << 16);   // BF16 magnitude -> FP32 bits
+}
+
+template <int FMT>
+__global__ void k_scale_from_amax(const float* __restrict__ amax, float* scale, float* scale_inv) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    float s = scale_from_amax<FMT>(*amax);
+    if (scale) *scale = s;
+    if (scale_inv) *scale_inv = 1.0f / s;
+  }
+}
+
+// Per-tensor cast without a transposed copy: 16 elements per thread and step
+// (two 16-byte loads, one 16-byte store).  n16 = number of 16-element groups.
+template <int FMT, bool AMAX>
+__global__ __launch_bounds__(kThreads) void k_cast(const uint4* __restrict__ x, int64_t n16,
+                                                   const float* __restrict__ scale_p,
+                                                   uint4* __restrict__ q,
+                                                   uint32_t* __restrict__ amax_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const float s = *scale_p;
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+    uint4 a = ld_stream(&x[2 * i]);
+    uint4 b = ld_stream(&x[2 * i + 1]);
+    if (AMAX) m = max(m, max(absmax8(a), absmax8(b)));
+    uint2 qa = cast8<FMT>(a, s), qb = cast8<FMT>(b, s);
+    uint4 o;
+    o.x = qa.x; o.y = qa.y; o.z = qb.x; o.w = qb.y;
+    q[i] = o;
+  }
+  if (AMAX) {
+    m = block_max_u32<kThreads>(m, red);
+    if (threadIdx.x == 0) atomicMax(amax_out, m << 16);
+  }
+}
+
+// 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
+// into columns: out[i] = bytes (a_i, b_i, c_i, d_i).
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                             uint32_t out[4]) {
+  uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  uint32_t t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  uint32_t t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);     // a0 b0 c0 d0
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);     // a1 b1 c1 d1
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Per-tensor cast with the transposed copy.  A 256-thread block owns a tile of
+// 128 rows x 128 columns; thread (tr, tc) = (t / 16, t % 16) owns the 8x8
+// sub-block at rows 8*tr.., columns 8*tc..  Loads: 16 lanes read 256
+// contiguous bytes of a row.  q rows are written 8 bytes per lane (128
+// contiguous bytes per 16 lanes); the 8x8 byte block is transposed in
+// registers and written to qT as 8 bytes per column.  Requires cols % 16 == 0
+// and rows % 16 == 0 (so row groups of 8 are never split by the edge).
+template <int FMT, bool AMAX>
+__global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict__ x, int64_t rows,
+                                                     int64_t cols,
+                                                     const float* __restrict__ scale_p,
+                                                     uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ qT,
+                                                     uint32_t* __restrict__ amax_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const float s = *scale_p;
+  const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * 128 + tr * 8;
+  const int64_t c0 = (int64_t)blockIdx.x * 128 + tc * 8;
+  uint32_t m = 0;
+  if (r0 < rows && c0 < cols) {
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 v = ld_stream((x + (r0 + i) * cols + c0));
+      if (AMAX) m = max(m, absmax8(v));
+      uint2 b = cast8<FMT>(v, s);
+      lo[i] = b.x;
+      hi[i] = b.y;
+      *(uint2*)(q + (r0 + i) * cols + c0) = b;
+    }
+    uint32_t tl[4], th[4], bl[4], bh[4];
+    transpose4x4(lo[0], lo[1], lo[2], lo[3], tl);   // columns 0-3, rows 0-3
+    transpose4x4(lo[4], lo[5], lo[6], lo[7], bl);   // columns 0-3, rows 4-7
+    transpose4x4(hi[0], hi[1], hi[2], hi[3], th);   // columns 4-7, rows 0-3
+    transpose4x4(hi[4], hi[5], hi[6], hi[7], bh);   // columns 4-7, rows 4-7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *(uint2*)(qT + (c0 + j) * rows + r0) = make_uint2(tl[j], bl[j]);
+      *(uint2*)(qT + (c0 + 4 + j) * rows + r0) = make_uint2(th[j], bh[j]);
+    }
+  }
+  if (AMAX) {
+    m = block_max_u32<kThreads>(m, red);
+    if (threadIdx.x == 0) atomicMax(amax_out, m << 16);
+  }
+}
+
+// Delayed-scaling step (one block of 256 threads).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_history(float* __restrict__ hist, int hlen,
+                                                      int64_t step,
+                                                      const float* __restrict__ amax,
+                                                      float* __restrict__ scale,
+                                                      float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int slot = (int)(step % hlen);
+  const float a = *amax;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < hlen; i += kThreads) {
+    float v = (i == slot) ? a : hist[i];
+    m = max(m, __float_as_uint(v) & 0x7fffffffu);
+  }
+  m = block_max_u32<kThreads>(m, red);
+  if (threadIdx.x == 0) {
+    hist[slot] = a;
+    float s = scale_from_amax<FMT>(__uint_as_float(m));
+    *scale = s;
+    *scale_inv = 1.0f / s;
+  }
+}
+
+// Blockwise 1x128: tile t covers the 128 contiguous elements [128t, 128t+128)
+// (cols % 128 == 0), handled by 16 lanes with one 16-byte load each.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_block_1x128(const uint4* __restrict__ x,
+                                                          int64_t ntiles,
+                                                          uint2* __restrict__ q,
+                                                          float* __restrict__ sinv) {
+  const int sub = threadIdx.x & 15;
+  const int64_t tiles_per_step = (int64_t)gridDim.x * (kThreads / 16);
+  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4); t < ntiles;
+       t += tiles_per_step) {
+    uint4 v = ld_stream(&x[t * 16 + sub]);
+    uint32_t m = group_max_u32<16>(absmax8(v));
+    float s = scale_from_amax<FMT>(__uint_as_float(m << 16));
+    q[t * 16 + sub] = cast8<FMT>(v, s);
+    if (sub == 0) sinv[t] = 1.0f / s;
+  }
+}
+
+// Blockwise 128x128: one 256-thread block per tile, thread (tr, tc) owns the
+// 8x8 sub-block at rows 8*tr.., columns 8*tc.. (rows % 128 == cols % 128 == 0).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_block_128(const uint16_t* __restrict__ x,
+                                                        int64_t cols, uint8_t* __restrict__ q,
+                                                        float* __restrict__ sinv) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * 128 + tr * 8;
+  const int64_t c0 = (int64_t)blockIdx.x * 128 + tc * 8;
+  uint4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = ld_stream((x + (r0 + i) * cols + c0));
+    m = max(m, absmax8(v[i]));
+  }
+  m = block_max_u32<kThreads>(m, red);
+  const float s = scale_from_amax<FMT>(__uint_as_float(m << 16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *(uint2*)(q + (r0 + i) * cols + c0) = cast8<FMT>(v[i], s);
+  if (threadIdx.x == 0) sinv[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = 1.0f / s;
+}
+
+// MX 1x32: block b covers elements [32b, 32b+32) (cols % 32 == 0), handled by
+// 4 lanes with one 16-byte load each.  The shared exponent is computed with
+// integer operations on the FP32 bits of the block's BF16 amax a:
+//   a = (1 + f) * 2^(E-127) with biased exponent E and fraction f; writing
+//   fmax = 1.75 * 2^P (P = 8 for E4M3, 15 for E5M2), the smallest integer e
+//   with a <= fmax * 2^e is (E - 127) - P when 1 + f <= 1.75 (fraction field
+//   <= 0x600000), else one more; clamped to [-127, 127].  Subnormal amax
+//   (E = 0) is far below fmax * 2^-127 and gets -127.
+template <int FMT>
+__device__ __forceinline__ int mx_exponent_bits(uint32_t abits) {
+  const int E = (int)(abits >> 23);
+  const uint32_t frac = abits & 0x7fffffu;
+  int e = (E - 127) - FmtTraits<FMT>::max_exp + (frac > 0x600000u ? 1 : 0);
+  if (E == 0) e = -127;
+  return min(127, max(-127, e));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_mx(const uint4* __restrict__ x, int64_t nblocks,
+                                                 uint2* __restrict__ q,
+                                                 uint8_t* __restrict__ e8m0) {
+  const int sub = threadIdx.x & 3;
+  const int64_t per_step = (int64_t)gridDim.x * (kThreads / 4);
+  for (int64_t b = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2); b < nblocks;
+       b += per_step) {
+    uint4 v = ld_stream(&x[b * 4 + sub]);
+    const uint32_t m = group_max_u32<4>(absmax8(v));   // BF16 magnitude bits
+    int e;
+    uint32_t byte;
+    if (m >= 0x7f80u) {            // inf or NaN in the block
+      e = 0;
+      byte = 0xffu;
+    } else if (m == 0u) {
+      e = 0;
+      byte = 127u;
+    } else {
+      e = mx_exponent_bits<FMT>(m << 16);
+      byte = (uint32_t)(e + 127);
+    }
+    const float s = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 120]
+    q[b * 4 + sub] = cast8<FMT>(v, s);
+    if (sub == 0) e8m0[b] = (uint8_t)byte;
+  }
+}
+
+// FP32 -> FP8 codes, 4 per thread, plus a scalar tail in block 0.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_convert(const float4* __restrict__ x, int64_t n4,
+                                                      const float* __restrict__ tail, int ntail,
+                                                      uint32_t* __restrict__ q,
+                                                      uint8_t* __restrict__ qtail) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+    float4 v = x[i];
+    q[i] = cvt4<FMT>(v.x, v.y, v.z, v.w);
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
+    qtail[threadIdx.x] = (uint8_t)(cvt4<FMT>(tail[threadIdx.x], 0.f, 0.f, 0.f) & 0xffu);
+}
+
+int grid_for(int64_t work_items, int per_block) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  int64_t cap = (int64_t)device_cu_count() * 8;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+#define FP8SG_FMT_DISPATCH(fmt, ...)                   \
+  do {                                                 \
+    if ((fmt) == kE4M3) {                              \
+      constexpr int F = kE4M3;                         \
+      __VA_ARGS__;                                     \
+    } else {                                           \
+      constexpr int F = kE5M2;                         \
+      __VA_ARGS__;                                     \
+    }                                                  \
+  } while (0)
+
+hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
+                       float* scale_inv, hipStream_t s) {
+  uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, out, 0u);
+  const int64_t nvec = n / 8;
+  const int ntail = (int)(n - nvec * 8);
+  const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
+  if (n > 0)
+    hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec > 0 ? nvec : 1, kThreads * 4)),
+                       dim3(kThreads), 0, s, static_cast<const uint4*>(x), nvec, tail, ntail,
+                       out);
+  if (scale || scale_inv)
+    FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_scale_from_amax<F>, dim3(1), dim3(64), 0, s,
+                                               amax, scale, scale_inv));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
+                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                  hipStream_t s) {
+  uint32_t* am = reinterpret_cast<uint32_t*>(amax_out);
+  if (am) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, am, 0u);
+  const int64_t n = rows * cols;
+  if (n == 0) return hipGetLastError();
+  if (qT) {
+    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+    FP8SG_FMT_DISPATCH(fmt, {
+      if (am)
+        hipLaunchKernelGGL((k_cast_t<F, true>), grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(x), rows, cols, scale, q, qT, am);
+      else
+        hipLaunchKernelGGL((k_cast_t<F, false>), grid, dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(x), rows, cols, scale, q, qT, am);
+    });
+  } else {
+    const int64_t n16 = n / 16;
+    const int g = grid_for(n16, kThreads * 4);
+    FP8SG_FMT_DISPATCH(fmt, {
+      if (am)
+        hipLaunchKernelGGL((k_cast<F, true>), dim3(g), dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), n16, scale,
+                           reinterpret_cast<uint4*>(q), am);
+      else
+        hipLaunchKernelGGL((k_cast<F, false>), dim3(g), dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), n16, scale,
+                           reinterpret_cast<uint4*>(q), am);
+    });
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
+                                 float* scale, float* scale_inv, hipStream_t s) {
+  FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_history<F>, dim3(1), dim3(kThreads), 0, s, hist,
+                                             hlen, step, amax, scale, scale_inv));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,
+                                 uint8_t* q, float* scale_inv, hipStream_t s) {
+  if (rows * cols == 0) return hipSuccess;
+  if (br == 1) {
+    const int64_t ntiles = rows * (cols / 128);
+    const int g = grid_for(ntiles, (kThreads / 16) * 4);
+    FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_1x128<F>, dim3(g), dim3(kThreads), 0, s,
+                                               static_cast<const uint4*>(x), ntiles,
+                                               reinterpret_cast<uint2*>(q), scale_inv));
+  } else {
+    dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+    FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_128<F>, grid, dim3(kThreads), 0, s,
+                                               static_cast<const uint16_t*>(x), cols, q,
+                                               scale_inv));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                              uint8_t* e8m0, hipStream_t s) {
+  const int64_t nblocks = rows * (cols / 32);
+  if (nblocks == 0) return hipSuccess;
+  const int g = grid_for(nblocks, (kThreads / 4) * 4);
+  FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_mx<F>, dim3(g), dim3(kThreads), 0, s,
+                                             static_cast<const uint4*>(x), nblocks,
+                                             reinterpret_cast<uint2*>(q), e8m0));
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t n4 = n / 4;
+  const int ntail = (int)(n - n4 * 4);
+  const int g = grid_for(n4 > 0 ? n4 : 1, kThreads * 4);
+  FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_convert<F>, dim3(g), dim3(kThreads), 0, s,
+                                             reinterpret_cast<const float4*>(x), n4,
+                                             x + n4 * 4, ntail,
+                                             reinterpret_cast<uint32_t*>(q), q + n4 * 4));
+  return hipGetLastError();
+}
+
+}  // namespace fp8sg

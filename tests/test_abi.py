@@ -1,0 +1,121 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/fp8sg.h declares, and rejects bad arguments with the
+documented status before anything is launched (the pointers below are never
+dereferenced: every call fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8sg.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, HIP = 0, 1, 2, 3, 4, 5
+P = 0x10000          # a 16-byte-aligned fake device address
+PU = 0x10001         # a misaligned one
+
+
+@pytest.fixture(scope="module")
+def L():
+    from scaled_fp8_gemm_amd import fp8sg
+    return fp8sg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:fp8_status_t|const char\*)\s+(fp8_\w+)\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    from scaled_fp8_gemm_amd import fp8sg
+    for code, name in fp8sg.STATUS.items():
+        assert fp8sg.fp8_status_string(code).startswith(name)
+
+
+def test_amax_errors(L):
+    assert L.fp8_amax(None, 4, 16, 0, P, None, None, None) == NULL
+    assert L.fp8_amax(P, 4, 16, 0, None, None, None, None) == NULL
+    assert L.fp8_amax(P, 4, 16, 7, P, None, None, None) == UNSUP
+    assert L.fp8_amax(P, -1, 16, 0, P, None, None, None) == SHAPE
+    assert L.fp8_amax(PU, 4, 16, 0, P, None, None, None) == ALIGN
+    assert L.fp8_amax(P, 4, 16, 0, P + 2, None, None, None) == ALIGN
+
+
+def test_quantize_tensor_errors(L):
+    q = L.fp8_quantize_tensor
+    assert q(None, 4, 16, 0, P, P, None, None, None) == NULL
+    assert q(P, 4, 16, 0, None, P, None, None, None) == NULL
+    assert q(P, 4, 16, 0, P, None, None, None, None) == NULL
+    assert q(P, 4, 16, 2, P, P, None, None, None) == UNSUP
+    assert q(P, 4, -16, 0, P, P, None, None, None) == SHAPE
+    assert q(P, 4, 24, 0, P, P, None, None, None) == ALIGN          # cols % 16
+    assert q(P, 8, 16, 0, P, P, P, None, None) == ALIGN             # qT needs rows % 16
+    assert q(PU, 16, 16, 0, P, P, None, None, None) == ALIGN
+
+
+def test_history_errors(L):
+    h = L.fp8_amax_history_update
+    assert h(None, 16, 0, P, 0, P, P, None) == NULL
+    assert h(P, 16, 0, P, 0, None, P, None) == NULL
+    assert h(P, 0, 0, P, 0, P, P, None) == SHAPE
+    assert h(P, 1025, 0, P, 0, P, P, None) == SHAPE
+    assert h(P, 16, -1, P, 0, P, P, None) == SHAPE
+    assert h(P, 16, 0, P, 5, P, P, None) == UNSUP
+
+
+def test_block_and_mx_errors(L):
+    b = L.fp8_quantize_block
+    assert b(P, 128, 256, 0, 2, 128, P, P, None) == UNSUP            # block_rows
+    assert b(P, 128, 256, 0, 1, 64, P, P, None) == UNSUP             # block_cols
+    assert b(P, 128, 200, 0, 1, 128, P, P, None) == SHAPE            # cols % 128
+    assert b(P, 100, 256, 0, 128, 128, P, P, None) == SHAPE          # rows % 128
+    assert b(None, 128, 256, 0, 1, 128, P, P, None) == NULL
+    m = L.fp8_quantize_mx
+    assert m(P, 4, 48, 0, P, P, None) == SHAPE                        # cols % 32
+    assert m(P, 4, 64, 0, None, P, None) == NULL
+    assert m(PU, 4, 64, 0, P, P, None) == ALIGN
+
+
+def _op(fmt, scaling, data=P, s=P):
+    from scaled_fp8_gemm_amd import fp8sg
+    return fp8sg.Operand(data, fmt, scaling, s)
+
+
+def test_gemm_errors(L):
+    g = L.fp8_gemm_fprop
+    r = ctypes.byref
+    t = _op(0, 0)
+    assert g(None, r(t), 16, 16, 16, P, None) == NULL
+    assert g(r(t), r(t), 16, 16, 16, None, None) == NULL
+    assert g(r(_op(0, 0, data=None)), r(t), 16, 16, 16, P, None) == NULL
+    assert g(r(_op(0, 0, s=None)), r(t), 16, 16, 16, P, None) == NULL
+    assert g(r(_op(3, 0)), r(t), 16, 16, 16, P, None) == UNSUP
+    assert g(r(_op(0, 9)), r(t), 16, 16, 16, P, None) == UNSUP
+    assert g(r(_op(0, 1)), r(t), 16, 16, 128, P, None) == UNSUP       # block x tensor
+    assert g(r(_op(0, 3)), r(_op(0, 1)), 16, 16, 128, P, None) == UNSUP
+    assert g(r(t), r(t), -1, 16, 16, P, None) == SHAPE
+    assert g(r(t), r(t), 16, 16, 24, P, None) == ALIGN                # K % 16
+    assert g(r(_op(0, 1)), r(_op(0, 2)), 16, 128, 64, P, None) == SHAPE   # K % 128
+    assert g(r(_op(0, 1)), r(_op(0, 2)), 16, 100, 128, P, None) == SHAPE  # 128x128 rows
+    assert g(r(_op(0, 3)), r(_op(0, 3)), 16, 16, 48, P, None) == SHAPE    # K % 32
+    assert g(r(t), r(t), 16, 16, 16, PU, None) == ALIGN
+    assert g(r(_op(0, 0, data=PU)), r(t), 16, 16, 16, P, None) == ALIGN
+    # dgrad contracts over N, wgrad over M
+    assert L.fp8_gemm_dgrad(r(t), r(t), 16, 24, 16, P, None) == ALIGN
+    assert L.fp8_gemm_wgrad(r(t), r(t), 24, 16, 16, P, None) == ALIGN
+
+
+def test_convert_errors(L):
+    c = L.fp8_convert_f32
+    assert c(None, 4, 0, P, None) == NULL
+    assert c(P, -1, 0, P, None) == SHAPE
+    assert c(P, 4, 3, P, None) == UNSUP
+    assert c(PU, 4, 0, P, None) == ALIGN

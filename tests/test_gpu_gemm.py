@@ -1,0 +1,146 @@
+"""GPU parity of the scaled FP8 GEMMs at sizes that span several 256x256
+tiles and ragged edges: every output element against the oracle, within the
+MFMA error bound derived in tests/gpu_helpers.py.  Random-code operands span
+the whole FP8 range (the worst case for the MFMA's aligned sum); the layer
+test uses quantised Gaussian data and also holds the 2-ulp typical bar."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import DEV, bits16, bytes8, check_gemm, dev_bf16, dev_f32, dev_u8, f32
+from tests.test_gpu_quant import rand_bits
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+TENSOR, B1, B128, MX = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def F():
+    from scaled_fp8_gemm_amd import fp8sg
+    fp8sg.lib()
+    return fp8sg
+
+
+def rand_codes(shape, fmt, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = rng.integers(0, 256, size=shape, dtype=np.int64).astype(np.uint8)
+    bad = (c & 0x7F) == 0x7F if fmt == E4M3 else (c & 0x7C) == 0x7C
+    c[bad] = 0x38 if fmt == E4M3 else 0x3C
+    return c
+
+
+def run_gemm(F, which, A, B, fa, fb, sca, scb, sa, sb, M, N, K):
+    """Call fprop / dgrad / wgrad on host arrays; returns output BF16 bits."""
+    Ad, Bd = dev_u8(A), dev_u8(B)
+    sad = dev_u8(sa) if sca == MX else dev_f32(sa)
+    sbd = dev_u8(sb) if scb == MX else dev_f32(sb)
+    oa = F.operand(Ad, fa, sca, sad)
+    ob = F.operand(Bd, fb, scb, sbd)
+    shape = {"fprop": (M, N), "dgrad": (M, K), "wgrad": (N, K)}[which]
+    out = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    getattr(F, f"fp8_gemm_{which}")(oa, ob, M, N, K, out)
+    torch.cuda.synchronize()
+    return bits16(out)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (600, 520, 400), (17, 33, 16), (1, 1, 128),
+                                   (513, 257, 1024), (300, 700, 2048)])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+def test_tensor_scaled(F, orc, M, N, K, fa, fb):
+    A = rand_codes((M, K), fa, M + K)
+    B = rand_codes((N, K), fb, N + 3 * K)
+    sa = np.array([0.031], np.float32)
+    sb = np.array([1.7e-3], np.float32)
+    g = run_gemm(F, "fprop", A, B, fa, fb, TENSOR, TENSOR, sa, sb, M, N, K)
+    check_gemm(orc, g, A, B, fa, fb, 0, sa, sb, label=f"tensor {M}x{N}x{K} fmt {fa}{fb}")
+
+
+def test_empty_and_zero_k(F, orc):
+    one = np.ones(1, np.float32)
+    g = run_gemm(F, "fprop", np.zeros((0, 16), np.uint8), np.zeros((32, 16), np.uint8),
+                 E4M3, E4M3, TENSOR, TENSOR, one, one, 0, 32, 16)
+    assert g.size == 0
+    g = run_gemm(F, "fprop", np.zeros((16, 0), np.uint8), np.zeros((48, 0), np.uint8),
+                 E4M3, E4M3, TENSOR, TENSOR, one, one, 16, 48, 0)
+    assert np.all(g == 0)
+
+
+@pytest.mark.parametrize("sca,scb", [(B1, B128), (B1, B1), (B128, B1), (B128, B128)])
+@pytest.mark.parametrize("M,N,K", [(640, 512, 384), (256, 384, 1024), (128, 128, 128)])
+def test_block_scaled(F, orc, sca, scb, M, N, K):
+    A = rand_codes((M, K), E4M3, 5 + M)
+    B = rand_codes((N, K), E4M3, 6 + N)
+    rng = np.random.Generator(np.random.PCG64(M * N))
+    bra = 1 if sca == B1 else 128
+    brb = 1 if scb == B1 else 128
+    sa = (10.0 ** rng.uniform(-4, 1, size=(M // bra, K // 128))).astype(np.float32)
+    sb = (10.0 ** rng.uniform(-4, 1, size=(N // brb, K // 128))).astype(np.float32)
+    g = run_gemm(F, "fprop", A, B, E4M3, E4M3, sca, scb, sa, sb, M, N, K)
+    check_gemm(orc, g, A, B, E4M3, E4M3, 1, sa, sb, bra, brb, label=f"block {sca}{scb} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(600, 520, 352), (256, 256, 256), (40, 1000, 4096)])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)])
+def test_mx_scaled(F, orc, M, N, K, fa, fb):
+    A = rand_codes((M, K), fa, 7 + K)
+    B = rand_codes((N, K), fb, 8 + K)
+    rng = np.random.Generator(np.random.PCG64(M + N + K))
+    ea = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    eb = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    g = run_gemm(F, "fprop", A, B, fa, fb, MX, MX, ea, eb, M, N, K)
+    check_gemm(orc, g, A, B, fa, fb, 2, ea, eb, label=f"mx {M}x{N}x{K} fmt {fa}{fb}")
+
+
+def test_mx_nan_scale_and_distinct_block_scales(F, orc):
+    """Every 32-block has its own scale; a NaN scale (0xFF) poisons its row."""
+    M, N, K = 64, 48, 256
+    A = rand_codes((M, K), E4M3, 1)
+    B = rand_codes((N, K), E4M3, 2)
+    ea = (117 + (np.arange(M * (K // 32)) % 20)).astype(np.uint8).reshape(M, K // 32)
+    eb = (127 - (np.arange(N * (K // 32)) % 13)).astype(np.uint8).reshape(N, K // 32)
+    ea[5, 3] = 0xFF
+    g = run_gemm(F, "fprop", A, B, E4M3, E4M3, MX, MX, ea, eb, M, N, K)
+    C, _, _ = orc.gemm_full(A, B, E4M3, E4M3, orc.SCALE_MX, ea, eb)
+    assert np.all(np.isnan(C[5]))
+    check_gemm(orc, g, A, B, E4M3, E4M3, 2, ea, eb, label="mx distinct scales")
+
+
+@pytest.mark.parametrize("M,K,N", [(272, 384, 400), (512, 256, 768)])
+def test_layer_three_gemms(F, orc, M, K, N):
+    """Quantise X, W, dY on the GPU (per-tensor current scaling, transposed
+    copies), run fprop / dgrad / wgrad, compare each with the oracle."""
+    x = rand_bits((M, K), 1, 1.0)
+    w = rand_bits((N, K), 2, 0.02)
+    gr = rand_bits((M, N), 3, 1e-3)
+    out = {}
+    for name, t, fmt in (("x", x, E4M3), ("w", w, E4M3), ("g", gr, E5M2)):
+        td = dev_bf16(t)
+        R, C = t.shape
+        am, s, si = (torch.empty(1, dtype=torch.float32, device=DEV) for _ in range(3))
+        F.fp8_amax(td, fmt, am, s, si)
+        q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+        qT = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+        F.fp8_quantize_tensor(td, fmt, s, q, qT)
+        out[name] = (q, qT, si, fmt)
+        ws, wsi = orc.scale_from_amax(orc.amax(t), fmt)
+        wq, wqT, _ = orc.quantize_tensor(t, fmt, ws, transposed=True)
+        assert np.array_equal(bytes8(q), wq) and np.array_equal(bytes8(qT), wqT)
+        assert f32(si)[0] == wsi
+    (xq, xqT, xsi, _), (wq, wqT, wsi, _), (gq, gqT, gsi, _) = out["x"], out["w"], out["g"]
+    T = TENSOR
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(F.operand(xq, E4M3, T, xsi), F.operand(wq, E4M3, T, wsi), M, N, K, y)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_dgrad(F.operand(gq, E5M2, T, gsi), F.operand(wqT, E4M3, T, wsi), M, N, K, dx)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_wgrad(F.operand(gqT, E5M2, T, gsi), F.operand(xqT, E4M3, T, xsi), M, N, K, dw)
+    torch.cuda.synchronize()
+    sx, sw, sg = f32(xsi), f32(wsi), f32(gsi)
+    check_gemm(orc, bits16(y), bytes8(xq), bytes8(wq), E4M3, E4M3, 0, sx, sw, label="fprop",
+               realistic=True)
+    check_gemm(orc, bits16(dx), bytes8(gq), bytes8(wqT), E5M2, E4M3, 0, sg, sw, label="dgrad",
+               realistic=True)
+    check_gemm(orc, bits16(dw), bytes8(gqT), bytes8(xqT), E5M2, E4M3, 0, sg, sx, label="wgrad",
+               realistic=True)

@@ -1,0 +1,170 @@
+"""GPU parity of the quantise path: amax, scale pair, per-tensor cast (with
+transposed copy and fused amax), delayed-scaling history, blockwise and MX
+casts.  Every byte, scale and amax must equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import DEV, bits16, bytes8, dev_bf16, dev_f32, f32
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def F():
+    from scaled_fp8_gemm_amd import fp8sg
+    fp8sg.lib()
+    return fp8sg
+
+
+def rand_bits(shape, seed, scale=1.0, specials=False):
+    """BF16 bit patterns: scaled normals, optionally sprinkled with specials."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = (rng.standard_normal(shape) * scale).astype(np.float32)
+    b = ((f.view(np.uint32) + 0x7FFF + ((f.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    if specials and b.size >= 16:
+        flat = b.reshape(-1)
+        idx = rng.choice(flat.size, size=min(64, flat.size // 4), replace=False)
+        pool = np.array([0x0000, 0x8000, 0x0001, 0x8003, 0x007F, 0x7F7F, 0xFF7F, 0x3F80],
+                        np.uint16)
+        flat[idx] = pool[rng.integers(0, pool.size, size=idx.size)]
+    return b
+
+
+def empty_dev(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device=DEV)
+
+
+@pytest.mark.parametrize("shape", [(0, 0), (1, 1), (3, 5), (37, 41), (1000, 1000), (4096, 513)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_amax_and_scale(F, orc, shape, fmt):
+    x = rand_bits(shape, 1 + shape[0], 3.0, specials=True)
+    xd = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+    F.fp8_amax(xd, fmt, am, s, si)
+    want = orc.amax(x) if x.size else 0.0
+    ws, wsi = orc.scale_from_amax(want, fmt)
+    assert f32(am)[0].view(np.uint32) == np.float32(want).view(np.uint32)
+    assert f32(s)[0] == ws and f32(si)[0] == wsi
+
+
+def test_amax_special_values(F, orc):
+    for special, expect_nan in ((0x7FC0, True), (0xFF80, False), (0x7F80, False)):
+        x = rand_bits((64, 64), 5)
+        x[10, 20] = special
+        am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+        F.fp8_amax(dev_bf16(x), E4M3, am, s, si)
+        a = f32(am)[0]
+        assert np.isnan(a) == expect_nan and (expect_nan or np.isinf(a))
+        assert f32(s)[0] == 1.0 and f32(si)[0] == 1.0
+    # a BF16-subnormal amax: the quotient overflows and the scale clamps
+    x = np.zeros((8, 16), np.uint16)
+    x[3, 3] = 0x0001
+    am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+    F.fp8_amax(dev_bf16(x), E4M3, am, s, si)
+    ws, wsi = orc.scale_from_amax(orc.amax(x), E4M3)
+    assert f32(s)[0] == ws == np.finfo(np.float32).max and f32(si)[0] == wsi
+
+
+@pytest.mark.parametrize("shape,transposed", [((0, 16), False), ((1, 16), False),
+                                              ((37, 48), False), ((48, 400), True),
+                                              ((256, 256), True), ((272, 384), True),
+                                              ((2000, 1040), True), ((3, 4096), False)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fused_amax", [False, True])
+def test_quantize_tensor(F, orc, shape, transposed, fmt, fused_amax):
+    x = rand_bits(shape, 7 + shape[1], 2.0, specials=True)
+    xd = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    # a scale that saturates the largest values (as delayed scaling can)
+    scale = np.float32({E4M3: 448.0, E5M2: 57344.0}[fmt] / 3.0)
+    R, C = shape
+    q = empty_dev(shape, torch.uint8)
+    qT = empty_dev((C, R), torch.uint8) if transposed else None
+    am = empty_dev(1, torch.float32) if fused_amax else None
+    F.fp8_quantize_tensor(xd, fmt, dev_f32([scale]), q, qT, am)
+    wq, wqT, wam = orc.quantize_tensor(x, fmt, scale, transposed=transposed, want_amax=fused_amax)
+    assert np.array_equal(bytes8(q), wq)
+    if transposed:
+        assert np.array_equal(bytes8(qT), wqT)
+    if fused_amax:
+        assert f32(am)[0].view(np.uint32) == np.float32(wam).view(np.uint32)
+
+
+def test_history_sequence(F, orc):
+    H = 16
+    hist_d = torch.zeros(H, dtype=torch.float32, device=DEV)
+    hist = np.zeros(H, np.float32)
+    s, si = empty_dev(1, torch.float32), empty_dev(1, torch.float32)
+    rng = np.random.Generator(np.random.PCG64(3))
+    for t in range(45):
+        a = np.float32(rng.uniform(0.5, 100.0) if t != 7 else 5000.0)
+        if t == 30:
+            a = np.float32(np.nan)
+        F.fp8_amax_history_update(hist_d, t, dev_f32([a]), E5M2 if t % 2 else E4M3, s, si)
+        ws, wsi = orc.amax_history_update(hist, t, a, E5M2 if t % 2 else E4M3)
+        got = f32(hist_d)
+        assert np.array_equal(got.view(np.uint32), hist.view(np.uint32)), t
+        assert f32(s)[0] == ws and f32(si)[0] == wsi, t
+
+
+@pytest.mark.parametrize("shape,br", [((256, 384), 1), ((256, 384), 128), ((1, 128), 1),
+                                      ((384, 1024), 128), ((0, 256), 1), ((999, 640), 1)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_block(F, orc, shape, br, fmt):
+    x = rand_bits(shape, 11 + shape[0], 1.0, specials=True)
+    if x.size:
+        x[0, :128] = 0                                 # an all-zero tile
+    xd = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    R, C = shape
+    q = empty_dev(shape, torch.uint8)
+    si = empty_dev((R // br, C // 128), torch.float32)
+    F.fp8_quantize_block(xd, fmt, br, 128, q, si)
+    if x.size == 0:
+        return
+    wq, wsi = orc.quantize_block(x, fmt, br, 128)
+    assert np.array_equal(bytes8(q), wq)
+    assert np.array_equal(f32(si).view(np.uint32), wsi.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (33, 96), (128, 4096), (257, 1024)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_mx(F, orc, shape, fmt):
+    x = rand_bits(shape, 13 + shape[0], 4.0, specials=True)
+    R, C = shape
+    if R > 4:
+        x[1, 0:32] = 0                                 # zero block -> 127
+        x[2, 32] = 0x7FC0                              # NaN block -> 0xFF
+        x[3, 0:32] = 0x0001                            # BF16-subnormal block -> clamp -127
+        x[4, 0:32] = 0x7F7F                            # largest BF16 -> e = 120
+        x[4, 40] = 0xFF80                              # -inf block
+    q = empty_dev(shape, torch.uint8)
+    e = empty_dev((R, C // 32), torch.uint8)
+    F.fp8_quantize_mx(dev_bf16(x), fmt, q, e)
+    wq, we = orc.quantize_mx(x, fmt)
+    assert np.array_equal(bytes8(e), we)
+    assert np.array_equal(bytes8(q), wq)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_convert_every_fp32_pattern(F, orc, fmt):
+    """The cast's rounding routine on all 2^32 FP32 inputs, in 2^28 chunks."""
+    chunk = 1 << 28
+    base = torch.arange(chunk, dtype=torch.int64, device=DEV)
+    q = empty_dev(chunk, torch.uint8)
+    for lo in range(0, 1 << 32, chunk):
+        x = (base + lo).to(torch.int32) if lo + chunk <= (1 << 31) else \
+            (base + lo - (1 << 32)).to(torch.int32)
+        F.fp8_convert_f32(x.view(torch.float32), fmt, q)
+        got = bytes8(q)
+        want = orc.encode_bits_range(lo, lo + chunk, fmt)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (f"fmt {fmt}: {bad.size} mismatches in chunk {lo:#x}, first input "
+                               f"{lo + int(bad[0]):#010x}: gpu {got[bad[0]]:#04x} "
+                               f"oracle {want[bad[0]]:#04x}")
+    # ragged tail path (n % 4 != 0)
+    x = torch.tensor([1.0, -2.5, 1e9, float("nan"), 3e-3, -0.0, 7.0], device=DEV)
+    q = empty_dev(7, torch.uint8)
+    F.fp8_convert_f32(x, fmt, q)
+    assert np.array_equal(bytes8(q), orc.encode(x.cpu().numpy(), fmt))
