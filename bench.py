@@ -10,14 +10,21 @@ its BF16 copy every step (training keeps a BF16 master and an FP8 copy).
 
 Prints one JSON line: throughput = 2MNK / (time per step) in TFLOP/s, with
 the GEMM's roofline (its average duration from HIP events recorded around
-each GEMM launch on the launch stream) and the CPU oracle timed on a bounded
-sample of the same workload as a baseline.
+each GEMM launch on the launch stream), the algorithmic GB/s of every
+quantise pass (events around each call), and the CPU oracle timed on a
+bounded sample of the same workload as a baseline.  `roofline.traffic` is the
+GEMM's HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+kept under profiles/, scaled by the same counters' reading for a plain copy of
+known size; it is null when that summary is missing or was taken from another
+version of the GEMM source.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload c2|c3|c4|c5]
+    python bench.py --copy-calibration      # the plain copy the counters are scaled by
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,7 +46,52 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 << 20
+# file-name slug of each workload (profiles/ summaries are named by kernel + slug)
+SLUG = {"c2": "llama7b_upproj_4096x4096x11008", "c3": "qkv_block_8192x4096x12288",
+        "c4": "llama13b_step_8192x5120x13824", "c5": "gpt175b_mlp_mx_4096x12288x49152"}
+GEMM_SOURCE = os.path.join(ROOT, "scaled_fp8_gemm_amd", "csrc", "gemm.hip")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, five times: FETCH_SIZE and
+    WRITE_SIZE of this kernel give the counters' bytes per true byte."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def traffic_per_launch(workload):
+    """HBM bytes per GEMM launch from the committed counter summary, or None.
+
+    The summary (profiles/k_gemm_<slug>_traffic.txt) holds key = value
+    lines: gemm_source_sha256, fetch_kib, write_kib (per GEMM dispatch) and
+    copy_fetch_kib, copy_write_kib (per copy of COPY_BYTES)."""
+    path = os.path.join(ROOT, "profiles", f"k_gemm_{SLUG[workload]}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    with open(GEMM_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha:
+        return None
+    fetch_factor = float(kv["copy_fetch_kib"]) * 1024 / COPY_BYTES
+    write_factor = float(kv["copy_write_kib"]) * 1024 / COPY_BYTES
+    return (float(kv["fetch_kib"]) * 1024 / fetch_factor
+            + float(kv["write_kib"]) * 1024 / write_factor)
 
 
 class Path:
@@ -83,60 +135,85 @@ class Path:
             self.am = {r: f1() for r in "xwg"}
             self.flops = 3 * 2.0 * M * N * K
             self.t = 0
-        self.gemm_events = []
+        # label -> (kind, algorithmic bytes or FLOP per call, [(start, end) events])
+        self.calls = {}
 
     def step(self, record=False):
-        F, torch = self.F, self.torch
+        F = self.F
         M, K, N = self.M, self.K, self.N
-        rec = self.gemm_events if record else None
+        c = lambda label, kind, work, fn, *a: self._call(record, label, kind, work, fn, *a)
+        gemm = 2.0 * M * N * K
         r = self.cfg.recipe
         if r == "tensor":
-            F.fp8_amax(self.x, F.E4M3, self.xa, self.xs, self.xsi)
-            F.fp8_amax(self.w, F.E4M3, self.wa, self.ws, self.wsi)
-            F.fp8_quantize_tensor(self.x, F.E4M3, self.xs, self.xq)
-            F.fp8_quantize_tensor(self.w, F.E4M3, self.ws, self.wq)
-            self._gemm(rec, F.fp8_gemm_fprop,
-                       F.operand(self.xq, F.E4M3, F.SCALE_TENSOR, self.xsi),
-                       F.operand(self.wq, F.E4M3, F.SCALE_TENSOR, self.wsi), M, N, K, self.y)
+            c("amax X", "hbm", 2 * M * K, F.fp8_amax, self.x, F.E4M3, self.xa, self.xs, self.xsi)
+            c("amax W", "hbm", 2 * N * K, F.fp8_amax, self.w, F.E4M3, self.wa, self.ws, self.wsi)
+            c("cast X", "hbm", 3 * M * K, F.fp8_quantize_tensor, self.x, F.E4M3, self.xs, self.xq)
+            c("cast W", "hbm", 3 * N * K, F.fp8_quantize_tensor, self.w, F.E4M3, self.ws, self.wq)
+            c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop,
+              F.operand(self.xq, F.E4M3, F.SCALE_TENSOR, self.xsi),
+              F.operand(self.wq, F.E4M3, F.SCALE_TENSOR, self.wsi), M, N, K, self.y)
         elif r == "block":
-            F.fp8_quantize_block(self.x, F.E4M3, 1, 128, self.xq, self.xsi)
-            F.fp8_quantize_block(self.w, F.E4M3, 128, 128, self.wq, self.wsi)
-            self._gemm(rec, F.fp8_gemm_fprop,
-                       F.operand(self.xq, F.E4M3, F.SCALE_BLOCK_1x128, self.xsi),
-                       F.operand(self.wq, F.E4M3, F.SCALE_BLOCK_128x128, self.wsi),
-                       M, N, K, self.y)
+            c("block 1x128 X", "hbm", 3 * M * K + 4 * M * K // 128, F.fp8_quantize_block,
+              self.x, F.E4M3, 1, 128, self.xq, self.xsi)
+            c("block 128x128 W", "hbm", 3 * N * K + 4 * N * K // 16384, F.fp8_quantize_block,
+              self.w, F.E4M3, 128, 128, self.wq, self.wsi)
+            c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop,
+              F.operand(self.xq, F.E4M3, F.SCALE_BLOCK_1x128, self.xsi),
+              F.operand(self.wq, F.E4M3, F.SCALE_BLOCK_128x128, self.wsi), M, N, K, self.y)
         elif r == "mx":
-            F.fp8_quantize_mx(self.x, F.E4M3, self.xq, self.xe)
-            F.fp8_quantize_mx(self.w, F.E4M3, self.wq, self.we)
-            self._gemm(rec, F.fp8_gemm_fprop,
-                       F.operand(self.xq, F.E4M3, F.SCALE_MX_1x32, self.xe),
-                       F.operand(self.wq, F.E4M3, F.SCALE_MX_1x32, self.we), M, N, K, self.y)
+            c("mx X", "hbm", 3 * M * K + M * K // 32, F.fp8_quantize_mx,
+              self.x, F.E4M3, self.xq, self.xe)
+            c("mx W", "hbm", 3 * N * K + N * K // 32, F.fp8_quantize_mx,
+              self.w, F.E4M3, self.wq, self.we)
+            c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop,
+              F.operand(self.xq, F.E4M3, F.SCALE_MX_1x32, self.xe),
+              F.operand(self.wq, F.E4M3, F.SCALE_MX_1x32, self.we), M, N, K, self.y)
         else:
             T = F.SCALE_TENSOR
-            F.fp8_quantize_tensor(self.x, F.E4M3, self.sc["x"], self.xq, self.xqT, self.am["x"])
-            F.fp8_quantize_tensor(self.w, F.E4M3, self.sc["w"], self.wq, self.wqT, self.am["w"])
-            F.fp8_quantize_tensor(self.g, F.E5M2, self.sc["g"], self.gq, self.gqT, self.am["g"])
-            self._gemm(rec, F.fp8_gemm_fprop, F.operand(self.xq, F.E4M3, T, self.sci["x"]),
-                       F.operand(self.wq, F.E4M3, T, self.sci["w"]), M, N, K, self.y)
-            self._gemm(rec, F.fp8_gemm_dgrad, F.operand(self.gq, F.E5M2, T, self.sci["g"]),
-                       F.operand(self.wqT, F.E4M3, T, self.sci["w"]), M, N, K, self.dx)
-            self._gemm(rec, F.fp8_gemm_wgrad, F.operand(self.gqT, F.E5M2, T, self.sci["g"]),
-                       F.operand(self.xqT, F.E4M3, T, self.sci["x"]), M, N, K, self.dw)
+            c("cast+T+amax X", "hbm", 4 * M * K, F.fp8_quantize_tensor,
+              self.x, F.E4M3, self.sc["x"], self.xq, self.xqT, self.am["x"])
+            c("cast+T+amax W", "hbm", 4 * N * K, F.fp8_quantize_tensor,
+              self.w, F.E4M3, self.sc["w"], self.wq, self.wqT, self.am["w"])
+            c("cast+T+amax G", "hbm", 4 * M * N, F.fp8_quantize_tensor,
+              self.g, F.E5M2, self.sc["g"], self.gq, self.gqT, self.am["g"])
+            c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop,
+              F.operand(self.xq, F.E4M3, T, self.sci["x"]),
+              F.operand(self.wq, F.E4M3, T, self.sci["w"]), M, N, K, self.y)
+            c("gemm dgrad", "mfma", gemm, F.fp8_gemm_dgrad,
+              F.operand(self.gq, F.E5M2, T, self.sci["g"]),
+              F.operand(self.wqT, F.E4M3, T, self.sci["w"]), M, N, K, self.dx)
+            c("gemm wgrad", "mfma", gemm, F.fp8_gemm_wgrad,
+              F.operand(self.gqT, F.E5M2, T, self.sci["g"]),
+              F.operand(self.xqT, F.E4M3, T, self.sci["x"]), M, N, K, self.dw)
             for role, fmt in (("x", F.E4M3), ("w", F.E4M3), ("g", F.E5M2)):
-                F.fp8_amax_history_update(self.hist[role], self.t, self.am[role], fmt,
-                                          self.sc[role], self.sci[role])
+                c(f"history {role.upper()}", "hbm", 2 * 16 * 4, F.fp8_amax_history_update,
+                  self.hist[role], self.t, self.am[role], fmt, self.sc[role], self.sci[role])
             self.t += 1
 
-    def _gemm(self, rec, fn, a, b, M, N, K, out):
-        if rec is None:
-            fn(a, b, M, N, K, out)
+    def _call(self, record, label, kind, work, fn, *args):
+        if not record:
+            fn(*args)
             return
         e0 = self.torch.cuda.Event(enable_timing=True)
         e1 = self.torch.cuda.Event(enable_timing=True)
         e0.record()
-        fn(a, b, M, N, K, out)
+        fn(*args)
         e1.record()
-        rec.append((e0, e1))
+        self.calls.setdefault(label, (kind, work, []))[2].append((e0, e1))
+
+    def summary(self):
+        """Per call: average duration (ms) and achieved rate."""
+        out = {}
+        for label, (kind, work, evs) in self.calls.items():
+            ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+            if kind == "mfma":
+                out[label] = {"avg_ms": round(ms, 5), "TFLOP/s": round(work / ms / 1e9, 2),
+                              "frac_fp8_peak": round(work / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
+            else:
+                gbs = work / ms / 1e6
+                out[label] = {"avg_ms": round(ms, 5), "bytes": int(work), "GB/s": round(gbs, 1),
+                              "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        return out
 
 
 def cpu_baseline(key):
@@ -179,6 +256,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(the multi-GPU sharding is described, not built)"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     dev = torch.device("cuda:0")
     p = Path(args.workload, dev)
@@ -195,8 +275,9 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
     tflops = p.flops / (ms * 1e-3) / 1e12
-    gemm_ms = [a.elapsed_time(b) for a, b in p.gemm_events]
-    gemm_avg_ms = sum(gemm_ms) / len(gemm_ms)
+    calls = p.summary()
+    gemm_labels = [k for k, v in p.calls.items() if v[0] == "mfma"]
+    gemm_avg_ms = sum(calls[k]["avg_ms"] for k in gemm_labels) / len(gemm_labels)
     flops_per_launch = 2.0 * p.M * p.N * p.K
     achieved = flops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
     cfg = p.cfg
@@ -204,6 +285,10 @@ def main():
               "block": "blockwise 1x128 (X) / 128x128 (W), E4M3",
               "delayed": "delayed scaling H=16, fprop+dgrad+wgrad, E4M3 / E5M2 grads",
               "mx": "MXFP8 1x32 E8M0, E4M3"}[cfg.recipe]
+    kernel = {"tensor": "k_gemm<tensor> (FP8 MFMA GEMM, 16x16x128)",
+              "block": "k_gemm<block> (FP8 MFMA GEMM, per-128-K promotion)",
+              "delayed": "k_gemm<tensor> (fprop, dgrad, wgrad launches)",
+              "mx": "k_gemm_deep<mx> (block-scaled MFMA 32x32x64)"}[cfg.recipe]
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -219,10 +304,12 @@ def main():
         "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N, "recipe": recipe},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm (FP8 MFMA GEMM)",
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "avg_ms": round(gemm_avg_ms, 5), "traffic": None},
+                     "avg_ms": round(gemm_avg_ms, 5), "flop_per_launch": flops_per_launch,
+                     "traffic": traffic_per_launch(args.workload)},
+        "calls": calls,
     }
     if not args.no_cpu_baseline and args.workload in ("c2",):
         out["cpu_baseline"] = cpu_baseline(args.workload)

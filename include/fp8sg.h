@@ -20,8 +20,14 @@
  *
  * Conventions for every call
  *   Memory      Every pointer argument except `stream` is device memory owned by
- *               the caller.  The library allocates nothing and keeps no state
- *               between calls.  Tensors are dense and row-major.
+ *               the caller.  Tensors are dense and row-major.  The calls that
+ *               produce an amax (fp8_amax, fp8_quantize_tensor with amax_out)
+ *               reduce through an 8 KB buffer of partial maxima that the
+ *               library allocates (hipMalloc) on the first such call on each
+ *               (device, stream) pair and keeps until the process ends; calls
+ *               on one stream run in order and share it, calls on different
+ *               streams never do.  If that first allocation fails the call
+ *               returns FP8_ERR_HIP.  No other call allocates.
  *   Stream      `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *               enqueue kernels and return; nothing synchronises.  Outputs are
  *               valid once the stream has passed the call.

@@ -7,8 +7,15 @@
 // rules are restated in include/fp8sg.h.  All of these kernels are bound by
 // HBM bandwidth: every element is read once as BF16 (2 B) and written once per
 // FP8 copy (1 B); they use 16-byte vector loads, grid-stride loops sized to
-// the CU count, and reduce maxima as unsigned magnitude bits (exact, and
-// order-independent, so atomicMax gives the same result on every run).
+// the CU count, and reduce maxima as unsigned magnitude bits (exact and
+// order-independent).  A kernel that produces an amax writes one partial
+// maximum per workgroup into a small per-stream workspace and a one-block
+// finalize kernel reduces them; same-address device atomics from thousands of
+// workgroups serialise (about 10 ns each on MI355X) and would cost more than
+// the pass itself.
+#include <mutex>
+#include <vector>
+
 #include "fp8_device.h"
 #include "launch.h"
 
@@ -18,63 +25,110 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ void k_fill_u32(uint32_t* p, uint32_t v) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
-}
+// Workgroups of a partial-producing launch (the partial buffer's length).
+constexpr int kMaxPartials = 2048;
+
+// Streaming kernels walk the tensor in contiguous chunks of 16 KB per
+// workgroup (kChunkLoads 16-byte loads per thread in flight), chunk c going to
+// workgroup c mod gridDim.x; the last chunk is predicated.
+constexpr int kChunkLoads = 4;
 
 // amax over n BF16 values: nvec 16-byte vectors plus a tail of < 8 elements.
+// part[blockIdx.x] = the workgroup's largest BF16 magnitude (bits & 0x7fff).
 __global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ x, int64_t nvec,
                                                    const uint16_t* __restrict__ tail, int ntail,
-                                                   uint32_t* __restrict__ out) {
+                                                   uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
+  constexpr int U = kChunkLoads;
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
-    uint4 v0 = ld_stream(&x[i]);
-    uint4 v1 = ld_stream(&x[i + stride]);
-    uint4 v2 = ld_stream(&x[i + 2 * stride]);
-    uint4 v3 = ld_stream(&x[i + 3 * stride]);
-    m = max(m, max(max(absmax8(v0), absmax8(v1)), max(absmax8(v2), absmax8(v3))));
+  const int64_t nchunks = (nvec + kThreads * U - 1) / (kThreads * U);
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t i = c * (kThreads * U) + threadIdx.x;
+    if (i + (U - 1) * kThreads < nvec) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[i + u * kThreads]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
+    } else {
+      for (int u = 0; u < U; ++u)
+        if (i + u * kThreads < nvec) m = max(m, absmax8(ld_stream(&x[i + u * kThreads])));
+    }
   }
-  for (; i < nvec; i += stride) m = max(m, absmax8(x[i]));
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7fffu));
   m = block_max_u32<kThreads>(m, red);
-  if (threadIdx.x == 0) atomicMax(out, m << 16);   // BF16 magnitude -> FP32 bits
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
+// Reduce n partial maxima to the tensor's amax (a BF16 magnitude widened to
+// FP32 bits) and, where asked, the scale pair derived from it.
 template <int FMT>
-__global__ void k_scale_from_amax(const float* __restrict__ amax, float* scale, float* scale_inv) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    float s = scale_from_amax<FMT>(*amax);
-    if (scale) *scale = s;
-    if (scale_inv) *scale_inv = 1.0f / s;
+__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __restrict__ part,
+                                                            int n, float* __restrict__ amax,
+                                                            float* __restrict__ scale,
+                                                            float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, part[i]);
+  m = block_max_u32<kThreads>(m, red);
+  if (threadIdx.x == 0) {
+    const float a = __uint_as_float(m << 16);
+    *amax = a;
+    if (scale || scale_inv) {
+      const float s = scale_from_amax<FMT>(a);
+      if (scale) *scale = s;
+      if (scale_inv) *scale_inv = 1.0f / s;
+    }
   }
 }
 
-// Per-tensor cast without a transposed copy: 16 elements per thread and step
-// (two 16-byte loads, one 16-byte store).  n16 = number of 16-element groups.
+// Per-tensor cast without a transposed copy: a thread casts 16 elements (two
+// 16-byte loads, one 16-byte store) per group; n16 = number of 16-element
+// groups; chunks of kThreads * 2 groups (16 KB of input) per workgroup step.
+template <int FMT>
+__device__ __forceinline__ uint4 cast16(uint4 a, uint4 b, float s) {
+  uint2 qa = cast8<FMT>(a, s), qb = cast8<FMT>(b, s);
+  return make_uint4(qa.x, qa.y, qb.x, qb.y);
+}
+
 template <int FMT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void k_cast(const uint4* __restrict__ x, int64_t n16,
                                                    const float* __restrict__ scale_p,
                                                    uint4* __restrict__ q,
-                                                   uint32_t* __restrict__ amax_out) {
+                                                   uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
+  constexpr int U = kChunkLoads / 2;
   const float s = *scale_p;
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
-    uint4 a = ld_stream(&x[2 * i]);
-    uint4 b = ld_stream(&x[2 * i + 1]);
-    if (AMAX) m = max(m, max(absmax8(a), absmax8(b)));
-    uint2 qa = cast8<FMT>(a, s), qb = cast8<FMT>(b, s);
-    uint4 o;
-    o.x = qa.x; o.y = qa.y; o.z = qb.x; o.w = qb.y;
-    q[i] = o;
+  const int64_t nchunks = (n16 + kThreads * U - 1) / (kThreads * U);
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t i = c * (kThreads * U) + threadIdx.x;
+    if (i + (U - 1) * kThreads < n16) {
+      uint4 a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = ld_stream(&x[2 * (i + u * kThreads)]);
+        b[u] = ld_stream(&x[2 * (i + u * kThreads) + 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (AMAX) m = max(m, max(absmax8(a[u]), absmax8(b[u])));
+        q[i + u * kThreads] = cast16<FMT>(a[u], b[u], s);
+      }
+    } else {
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = i + u * kThreads;
+        if (j < n16) {
+          uint4 a0 = ld_stream(&x[2 * j]), b0 = ld_stream(&x[2 * j + 1]);
+          if (AMAX) m = max(m, max(absmax8(a0), absmax8(b0)));
+          q[j] = cast16<FMT>(a0, b0, s);
+        }
+      }
+    }
   }
   if (AMAX) {
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) atomicMax(amax_out, m << 16);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
   }
 }
 
@@ -92,27 +146,29 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
   out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-// Per-tensor cast with the transposed copy.  A 256-thread block owns a tile of
-// 128 rows x 128 columns; thread (tr, tc) = (t / 16, t % 16) owns the 8x8
-// sub-block at rows 8*tr.., columns 8*tc..  Loads: 16 lanes read 256
+// Per-tensor cast with the transposed copy.  The tensor is cut into tiles of
+// 128 rows x 128 columns, visited grid-stride (tile t: row tile t / ntx,
+// column tile t % ntx); in a tile, thread (tr, tc) = (t / 16, t % 16) owns the
+// 8x8 sub-block at rows 8*tr.., columns 8*tc..  Loads: 16 lanes read 256
 // contiguous bytes of a row.  q rows are written 8 bytes per lane (128
 // contiguous bytes per 16 lanes); the 8x8 byte block is transposed in
 // registers and written to qT as 8 bytes per column.  Requires cols % 16 == 0
 // and rows % 16 == 0 (so row groups of 8 are never split by the edge).
 template <int FMT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict__ x, int64_t rows,
-                                                     int64_t cols,
+                                                     int64_t cols, int64_t ntx, int64_t ntiles,
                                                      const float* __restrict__ scale_p,
                                                      uint8_t* __restrict__ q,
                                                      uint8_t* __restrict__ qT,
-                                                     uint32_t* __restrict__ amax_out) {
+                                                     uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
   const float s = *scale_p;
   const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
-  const int64_t r0 = (int64_t)blockIdx.y * 128 + tr * 8;
-  const int64_t c0 = (int64_t)blockIdx.x * 128 + tc * 8;
   uint32_t m = 0;
-  if (r0 < rows && c0 < cols) {
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t r0 = (t / ntx) * 128 + tr * 8;
+    const int64_t c0 = (t % ntx) * 128 + tc * 8;
+    if (r0 >= rows || c0 >= cols) continue;
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -136,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict_
   }
   if (AMAX) {
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) atomicMax(amax_out, m << 16);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
   }
 }
 
@@ -165,21 +221,39 @@ __global__ __launch_bounds__(kThreads) void k_history(float* __restrict__ hist, 
 }
 
 // Blockwise 1x128: tile t covers the 128 contiguous elements [128t, 128t+128)
-// (cols % 128 == 0), handled by 16 lanes with one 16-byte load each.
+// (cols % 128 == 0), handled by 16 lanes with one 16-byte load each; a lane
+// group keeps four tiles' loads in flight.
+template <int FMT>
+__device__ __forceinline__ void block_1x128_tile(uint4 v, int64_t t, int sub,
+                                                 uint2* __restrict__ q,
+                                                 float* __restrict__ sinv) {
+  const uint32_t m = group_max_u32<16>(absmax8(v));
+  const float s = scale_from_amax<FMT>(__uint_as_float(m << 16));
+  q[t * 16 + sub] = cast8<FMT>(v, s);
+  if (sub == 0) sinv[t] = 1.0f / s;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_block_1x128(const uint4* __restrict__ x,
                                                           int64_t ntiles,
                                                           uint2* __restrict__ q,
                                                           float* __restrict__ sinv) {
+  constexpr int U = kChunkLoads, G = kThreads / 16;   // G tiles per load step
   const int sub = threadIdx.x & 15;
-  const int64_t tiles_per_step = (int64_t)gridDim.x * (kThreads / 16);
-  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4); t < ntiles;
-       t += tiles_per_step) {
-    uint4 v = ld_stream(&x[t * 16 + sub]);
-    uint32_t m = group_max_u32<16>(absmax8(v));
-    float s = scale_from_amax<FMT>(__uint_as_float(m << 16));
-    q[t * 16 + sub] = cast8<FMT>(v, s);
-    if (sub == 0) sinv[t] = 1.0f / s;
+  const int64_t nchunks = (ntiles + G * U - 1) / (G * U);
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t t = c * (G * U) + (threadIdx.x >> 4);
+    if (t + (U - 1) * G < ntiles) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[(t + u * G) * 16 + sub]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) block_1x128_tile<FMT>(v[u], t + u * G, sub, q, sinv);
+    } else {
+      for (int u = 0; u < U; ++u)
+        if (t + u * G < ntiles)
+          block_1x128_tile<FMT>(ld_stream(&x[(t + u * G) * 16 + sub]), t + u * G, sub, q, sinv);
+    }
   }
 }
 
@@ -224,31 +298,48 @@ __device__ __forceinline__ int mx_exponent_bits(uint32_t abits) {
   return min(127, max(-127, e));
 }
 
+// One 32-element block held by 4 lanes (one 16-byte load each).
+template <int FMT>
+__device__ __forceinline__ void mx_block(uint4 v, int64_t b, int sub, uint2* __restrict__ q,
+                                         uint8_t* __restrict__ e8m0) {
+  const uint32_t m = group_max_u32<4>(absmax8(v));   // BF16 magnitude bits
+  int e;
+  uint32_t byte;
+  if (m >= 0x7f80u) {            // inf or NaN in the block
+    e = 0;
+    byte = 0xffu;
+  } else if (m == 0u) {
+    e = 0;
+    byte = 127u;
+  } else {
+    e = mx_exponent_bits<FMT>(m << 16);
+    byte = (uint32_t)(e + 127);
+  }
+  const float s = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 120]
+  q[b * 4 + sub] = cast8<FMT>(v, s);
+  if (sub == 0) e8m0[b] = (uint8_t)byte;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_mx(const uint4* __restrict__ x, int64_t nblocks,
                                                  uint2* __restrict__ q,
                                                  uint8_t* __restrict__ e8m0) {
+  constexpr int U = kChunkLoads, G = kThreads / 4;   // G blocks per load step
   const int sub = threadIdx.x & 3;
-  const int64_t per_step = (int64_t)gridDim.x * (kThreads / 4);
-  for (int64_t b = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2); b < nblocks;
-       b += per_step) {
-    uint4 v = ld_stream(&x[b * 4 + sub]);
-    const uint32_t m = group_max_u32<4>(absmax8(v));   // BF16 magnitude bits
-    int e;
-    uint32_t byte;
-    if (m >= 0x7f80u) {            // inf or NaN in the block
-      e = 0;
-      byte = 0xffu;
-    } else if (m == 0u) {
-      e = 0;
-      byte = 127u;
+  const int64_t nchunks = (nblocks + G * U - 1) / (G * U);
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t b = c * (G * U) + (threadIdx.x >> 2);
+    if (b + (U - 1) * G < nblocks) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[(b + u * G) * 4 + sub]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx_block<FMT>(v[u], b + u * G, sub, q, e8m0);
     } else {
-      e = mx_exponent_bits<FMT>(m << 16);
-      byte = (uint32_t)(e + 127);
+      for (int u = 0; u < U; ++u)
+        if (b + u * G < nblocks)
+          mx_block<FMT>(ld_stream(&x[(b + u * G) * 4 + sub]), b + u * G, sub, q, e8m0);
     }
-    const float s = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 120]
-    q[b * 4 + sub] = cast8<FMT>(v, s);
-    if (sub == 0) e8m0[b] = (uint8_t)byte;
   }
 }
 
@@ -267,12 +358,45 @@ __global__ __launch_bounds__(kThreads) void k_convert(const float4* __restrict__
     qtail[threadIdx.x] = (uint8_t)(cvt4<FMT>(tail[threadIdx.x], 0.f, 0.f, 0.f) & 0xffu);
 }
 
+// Workgroups for a grid-stride launch: enough for the work, at most eight per
+// CU and never more than the partial buffer holds.
 int grid_for(int64_t work_items, int per_block) {
   int64_t g = (work_items + per_block - 1) / per_block;
   int64_t cap = (int64_t)device_cu_count() * 8;
+  if (cap > kMaxPartials) cap = kMaxPartials;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   return (int)g;
+}
+
+// One partial-maximum buffer (kMaxPartials words) per (device, stream),
+// allocated on first use and kept until the process ends.  Work on one stream
+// runs in order, so successive calls on a stream share its buffer safely;
+// calls on different streams never share one.
+struct StreamBuffer {
+  int dev;
+  hipStream_t stream;
+  uint32_t* p;
+};
+std::mutex g_partials_mu;
+std::vector<StreamBuffer> g_partials;
+
+hipError_t stream_partials(hipStream_t s, uint32_t** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_partials_mu);
+  for (const StreamBuffer& b : g_partials)
+    if (b.dev == dev && b.stream == s) {
+      *out = b.p;
+      return hipSuccess;
+    }
+  void* p = nullptr;
+  err = hipMalloc(&p, kMaxPartials * sizeof(uint32_t));
+  if (err != hipSuccess) return err;
+  g_partials.push_back({dev, s, static_cast<uint32_t*>(p)});
+  *out = static_cast<uint32_t*>(p);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -304,52 +428,64 @@ int device_cu_count() {
 
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
                        float* scale_inv, hipStream_t s) {
-  uint32_t* out = reinterpret_cast<uint32_t*>(amax);
-  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, out, 0u);
+  uint32_t* part = nullptr;
+  hipError_t err = stream_partials(s, &part);
+  if (err != hipSuccess) return err;
   const int64_t nvec = n / 8;
   const int ntail = (int)(n - nvec * 8);
   const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
-  if (n > 0)
-    hipLaunchKernelGGL(k_amax, dim3(grid_for(nvec > 0 ? nvec : 1, kThreads * 4)),
-                       dim3(kThreads), 0, s, static_cast<const uint4*>(x), nvec, tail, ntail,
-                       out);
-  if (scale || scale_inv)
-    FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_scale_from_amax<F>, dim3(1), dim3(64), 0, s,
-                                               amax, scale, scale_inv));
+  int g = 1;
+  if (n > 0) {
+    g = grid_for(nvec > 0 ? nvec : 1, kThreads * kChunkLoads);
+    hipLaunchKernelGGL(k_amax, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(x),
+                       nvec, tail, ntail, part);
+  }
+  FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,
+                                             part, n > 0 ? g : 0, amax, scale, scale_inv));
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                   hipStream_t s) {
-  uint32_t* am = reinterpret_cast<uint32_t*>(amax_out);
-  if (am) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, am, 0u);
+  uint32_t* part = nullptr;
+  if (amax_out) {
+    hipError_t err = stream_partials(s, &part);
+    if (err != hipSuccess) return err;
+  }
   const int64_t n = rows * cols;
-  if (n == 0) return hipGetLastError();
-  if (qT) {
-    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+  int g = 0;
+  if (n > 0 && qT) {
+    const int64_t ntx = (cols + 127) / 128;
+    const int64_t ntiles = ntx * ((rows + 127) / 128);
+    g = grid_for(ntiles, 1);
     FP8SG_FMT_DISPATCH(fmt, {
-      if (am)
-        hipLaunchKernelGGL((k_cast_t<F, true>), grid, dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(x), rows, cols, scale, q, qT, am);
+      if (part)
+        hipLaunchKernelGGL((k_cast_t<F, true>), dim3(g), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(x), rows, cols, ntx, ntiles, scale, q, qT,
+                           part);
       else
-        hipLaunchKernelGGL((k_cast_t<F, false>), grid, dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(x), rows, cols, scale, q, qT, am);
+        hipLaunchKernelGGL((k_cast_t<F, false>), dim3(g), dim3(kThreads), 0, s,
+                           static_cast<const uint16_t*>(x), rows, cols, ntx, ntiles, scale, q, qT,
+                           part);
     });
-  } else {
+  } else if (n > 0) {
     const int64_t n16 = n / 16;
-    const int g = grid_for(n16, kThreads * 4);
+    g = grid_for(n16, kThreads * (kChunkLoads / 2));
     FP8SG_FMT_DISPATCH(fmt, {
-      if (am)
+      if (part)
         hipLaunchKernelGGL((k_cast<F, true>), dim3(g), dim3(kThreads), 0, s,
                            static_cast<const uint4*>(x), n16, scale,
-                           reinterpret_cast<uint4*>(q), am);
+                           reinterpret_cast<uint4*>(q), part);
       else
         hipLaunchKernelGGL((k_cast<F, false>), dim3(g), dim3(kThreads), 0, s,
                            static_cast<const uint4*>(x), n16, scale,
-                           reinterpret_cast<uint4*>(q), am);
+                           reinterpret_cast<uint4*>(q), part);
     });
   }
+  if (part)
+    FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,
+                                               part, g, amax_out, nullptr, nullptr));
   return hipGetLastError();
 }
 
@@ -365,7 +501,7 @@ hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int 
   if (rows * cols == 0) return hipSuccess;
   if (br == 1) {
     const int64_t ntiles = rows * (cols / 128);
-    const int g = grid_for(ntiles, (kThreads / 16) * 4);
+    const int g = grid_for(ntiles, (kThreads / 16) * kChunkLoads);
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_1x128<F>, dim3(g), dim3(kThreads), 0, s,
                                                static_cast<const uint4*>(x), ntiles,
                                                reinterpret_cast<uint2*>(q), scale_inv));
@@ -382,7 +518,7 @@ hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt
                               uint8_t* e8m0, hipStream_t s) {
   const int64_t nblocks = rows * (cols / 32);
   if (nblocks == 0) return hipSuccess;
-  const int g = grid_for(nblocks, (kThreads / 4) * 4);
+  const int g = grid_for(nblocks, (kThreads / 4) * kChunkLoads);
   FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_mx<F>, dim3(g), dim3(kThreads), 0, s,
                                              static_cast<const uint4*>(x), nblocks,
                                              reinterpret_cast<uint2*>(q), e8m0));

@@ -18,8 +18,8 @@ device):
   round-to-nearest-even);
 * each tensor's seed is ``splitmix64(BASE_SEED ^ fnv1a64("<config>/<tensor>/<step>"))``.
 
-The workload table (shapes and distributions) follows the five graded
-configurations of this library; see ``CONFIGS``.
+The workload table (shapes and distributions of the five measured workloads)
+is ``CONFIGS``.
 """
 from __future__ import annotations
 

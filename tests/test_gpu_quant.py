@@ -37,7 +37,10 @@ def empty_dev(shape, dtype):
     return torch.empty(shape, dtype=dtype, device=DEV)
 
 
-@pytest.mark.parametrize("shape", [(0, 0), (1, 1), (3, 5), (37, 41), (1000, 1000), (4096, 513)])
+# (2056, 8208) spans more 16 KB chunks than the launch has workgroups, with a
+# ragged last chunk.
+@pytest.mark.parametrize("shape", [(0, 0), (1, 1), (3, 5), (37, 41), (1000, 1000), (4096, 513),
+                                   (2056, 8208)])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_amax_and_scale(F, orc, shape, fmt):
     x = rand_bits(shape, 1 + shape[0], 3.0, specials=True)
@@ -71,7 +74,9 @@ def test_amax_special_values(F, orc):
 @pytest.mark.parametrize("shape,transposed", [((0, 16), False), ((1, 16), False),
                                               ((37, 48), False), ((48, 400), True),
                                               ((256, 256), True), ((272, 384), True),
-                                              ((2000, 1040), True), ((3, 4096), False)])
+                                              ((2000, 1040), True), ((3, 4096), False),
+                                              # more chunks / tiles than workgroups, ragged
+                                              ((4112, 8208), False), ((4112, 8208), True)])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 @pytest.mark.parametrize("fused_amax", [False, True])
 def test_quantize_tensor(F, orc, shape, transposed, fmt, fused_amax):
@@ -110,7 +115,8 @@ def test_history_sequence(F, orc):
 
 
 @pytest.mark.parametrize("shape,br", [((256, 384), 1), ((256, 384), 128), ((1, 128), 1),
-                                      ((384, 1024), 128), ((0, 256), 1), ((999, 640), 1)])
+                                      ((384, 1024), 128), ((0, 256), 1), ((999, 640), 1),
+                                      ((2056, 8192), 1)])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_quantize_block(F, orc, shape, br, fmt):
     x = rand_bits(shape, 11 + shape[0], 1.0, specials=True)
@@ -128,7 +134,7 @@ def test_quantize_block(F, orc, shape, br, fmt):
     assert np.array_equal(f32(si).view(np.uint32), wsi.view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", [(1, 32), (33, 96), (128, 4096), (257, 1024)])
+@pytest.mark.parametrize("shape", [(1, 32), (33, 96), (128, 4096), (257, 1024), (2056, 8192)])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_quantize_mx(F, orc, shape, fmt):
     x = rand_bits(shape, 13 + shape[0], 4.0, specials=True)
