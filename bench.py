@@ -55,7 +55,17 @@ COPY_BYTES = 512 << 20
 # file-name slug of each workload (profiles/ summaries are named by kernel + slug)
 SLUG = {"c2": "llama7b_upproj_4096x4096x11008", "c3": "qkv_block_8192x4096x12288",
         "c4": "llama13b_step_8192x5120x13824", "c5": "gpt175b_mlp_mx_4096x12288x49152"}
-GEMM_SOURCE = os.path.join(ROOT, "scaled_fp8_gemm_amd", "csrc", "gemm.hip")
+# sources of the GEMM kernel the traffic counters describe
+GEMM_SOURCES = [os.path.join(ROOT, "scaled_fp8_gemm_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_common.h", "fp8_device.h")]
+
+
+def gemm_source_sha256():
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def copy_calibration():
@@ -73,10 +83,10 @@ def copy_calibration():
 def traffic_per_launch(workload):
     """HBM bytes per GEMM launch from the committed counter summary, or None.
 
-    The summary (profiles/k_gemm_<slug>_traffic.txt) holds key = value
+    The summary (profiles/k_gemm8_<slug>_traffic.txt) holds key = value
     lines: gemm_source_sha256, fetch_kib, write_kib (per GEMM dispatch) and
     copy_fetch_kib, copy_write_kib (per copy of COPY_BYTES)."""
-    path = os.path.join(ROOT, "profiles", f"k_gemm_{SLUG[workload]}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"k_gemm8_{SLUG[workload]}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -84,9 +94,7 @@ def traffic_per_launch(workload):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    with open(GEMM_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if kv.get("gemm_source_sha256") != sha:
+    if kv.get("gemm_source_sha256") != gemm_source_sha256():
         return None
     fetch_factor = float(kv["copy_fetch_kib"]) * 1024 / COPY_BYTES
     write_factor = float(kv["copy_write_kib"]) * 1024 / COPY_BYTES
@@ -285,10 +293,10 @@ def main():
               "block": "blockwise 1x128 (X) / 128x128 (W), E4M3",
               "delayed": "delayed scaling H=16, fprop+dgrad+wgrad, E4M3 / E5M2 grads",
               "mx": "MXFP8 1x32 E8M0, E4M3"}[cfg.recipe]
-    kernel = {"tensor": "k_gemm<tensor> (FP8 MFMA GEMM, 16x16x128)",
-              "block": "k_gemm<block> (FP8 MFMA GEMM, per-128-K promotion)",
-              "delayed": "k_gemm<tensor> (fprop, dgrad, wgrad launches)",
-              "mx": "k_gemm_deep<mx> (block-scaled MFMA 32x32x64)"}[cfg.recipe]
+    kernel = {"tensor": "k_gemm8<tensor> (FP8 MFMA 16x16x128, 8 waves, 256x256 tile)",
+              "block": "k_gemm8<block> (FP8 MFMA, per-128-K promotion on VALU)",
+              "delayed": "k_gemm8<tensor> (fprop, dgrad, wgrad launches)",
+              "mx": "k_gemm8<mx> (block-scaled MFMA 16x16x128, E8M0 operands)"}[cfg.recipe]
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),

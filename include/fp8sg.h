@@ -167,7 +167,7 @@ fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int
  *   MX     x MX    :  sum_t a(i,t) 2^ea(i,t/32) * b(j,t) 2^eb(j,t/32)
  * Shape rules: sizes >= 0; contraction % 16 == 0 (FP8_ERR_ALIGN); block
  * operands need contraction % 128 == 0 and, for 128x128, rows % 128 == 0; MX
- * needs contraction % 32 == 0 (FP8_ERR_SHAPE).  Mixed families are
+ * needs contraction % 32 == 0; contraction <= 2^23 (FP8_ERR_SHAPE).  Mixed families are
  * FP8_ERR_UNSUPPORTED.  Output pointers must be 16-byte aligned.
  * Errors: NULL operand/data/scale/output; shapes; alignment; enums. */
 fp8_status_t fp8_gemm_fprop(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,

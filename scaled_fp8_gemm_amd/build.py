@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8sg.so")
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "gemm_mx_k32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -16,6 +16,9 @@ using fp8sg::GemmProblem;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;           // rows / cols limit
 constexpr int64_t kMaxTileRows = (int64_t)65535 * 128;  // 2-D launch grid limit
+// GEMM contraction limit: the kernels address a 256-row operand tile with
+// 32-bit buffer offsets (256 * K < 2^31).
+constexpr int64_t kMaxContraction = (int64_t)1 << 23;
 
 bool fmt_ok(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -46,6 +49,7 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   else
     return FP8_ERR_UNSUPPORTED;
   if (!dims_ok(rows_a, kc) || !dims_ok(rows_b, kc)) return FP8_ERR_SHAPE;
+  if (kc > kMaxContraction) return FP8_ERR_SHAPE;
   const int64_t nc = rows_a * rows_b;
   if (!have(a->data, rows_a * kc) || !have(b->data, rows_b * kc) || !have(c, nc) ||
       !have(a->scale_inv, nc) || !have(b->scale_inv, nc))
@@ -100,7 +104,6 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
   if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
   if (!have(x_bf16, rows * cols) || !have(q, rows * cols) || !have(scale, rows * cols))
     return FP8_ERR_NULL;
-  if (qT && rows > kMaxTileRows) return FP8_ERR_SHAPE;
   if (cols % 16) return FP8_ERR_ALIGN;
   if (qT && rows % 16) return FP8_ERR_ALIGN;
   if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||

@@ -1,0 +1,196 @@
+// gemm_common.h -- pieces shared by the FP8 MFMA GEMM kernels of libfp8sg
+// (gfx950): kernel arguments, the XCD-aware tile order, LDS DMA of operand
+// tiles (buffer_load ... lds) and the 16x16x128 MFMA fragment reads.
+//
+// MFMA operand layout of v_mfma_*_16x16x128_f8f6f4 (measured on gfx950):
+// lane l holds row l%16 of its operand; bytes 0..15 hold K [16g, 16g+16) and
+// bytes 16..31 hold K [64+16g, 64+16g+16) of the 128-K step, with g = l/16.
+// The E8M0 scale of lane l applies to row l%16 and 32-K block l/16.  The 4
+// outputs of lane l are rows 4g..4g+3 of the first operand against row l%16
+// of the second.
+#pragma once
+
+#include "fp8_device.h"
+
+namespace fp8sg {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+enum : int { kTensor = 0, kBlock = 1, kMX = 2 };
+
+// Bytes of K per main-loop step of the BK = 128 kernels.
+constexpr int BK = 128;
+
+struct Args {
+  const uint8_t* A;
+  const uint8_t* B;
+  const void* sa;
+  const void* sb;
+  uint16_t* C;
+  int64_t M, N, K;
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// LDS byte address of a __shared__ pointer (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+// Buffer descriptor over `records` bytes from `base` (raw buffer, no stride,
+// range-checked: loads past `records` return zeros).
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t records) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) & 0xffff;
+  r[2] = (int)__builtin_amdgcn_readfirstlane(records);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voffset into LDS
+// at m0 + 16 * lane.  Issued through inline assembly so that the compiler
+// neither models it as an LDS write (which would make it wait for the load
+// before unrelated LDS reads of the other buffer) nor reorders it; completion
+// is awaited explicitly with vmcnt before the workgroup barrier.  m0 is
+// reserved by the compiler, so the sequence restores it.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voffset) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
+
+// The same with 4 bytes per lane (LDS at m0 + 4 * lane).
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voffset) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// 128-byte rows of a BK = 128 stage; 16-byte chunks XOR-swizzled by row so
+// the 16 rows a fragment read touches fall in different banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7)) << 4);
+}
+
+// Operand tile loader for BK = 128 stages.  A ROWS x 128-byte tile is ROWS/8
+// chunks of 8 rows (1 KB); with NW loading waves, wave w moves chunks
+// w*L .. w*L+L-1, L = ROWS / (8 * NW).  Lane l of a chunk lands at LDS byte
+// l*16 of it, i.e. row l/8 and physical 16-byte slot l%8, so it loads logical
+// chunk (l%8) ^ (row & 7) of that row.  The buffer descriptor covers exactly
+// the tile's valid rows, so the hardware range check zero-fills rows past the
+// matrix edge; lanes whose chunk lies past K are pointed at the end of the
+// range and get zeros too.  Offsets are 32-bit: the ABI keeps K <= 2^23.
+template <int ROWS, int NW>
+struct TileLoader {
+  static constexpr int L = ROWS / (8 * NW);
+  v4i rsrc;
+  uint32_t records;
+  int64_t K;
+  int voff[L];      // byte offset of this lane's chunk in each of its loads (k0 = 0)
+  int kchunk;       // logical 16-byte chunk this lane loads
+  int w;            // index of this wave among the NW loading waves
+
+  __device__ __forceinline__ void init(const uint8_t* base, int64_t rows_left, int64_t K_,
+                                       int wave) {
+    K = K_;
+    w = wave;
+    const int64_t rows = rows_left < ROWS ? rows_left : ROWS;
+    records = __builtin_amdgcn_readfirstlane((uint32_t)(rows * K));
+    rsrc = make_rsrc(base, records);
+    const int lane = threadIdx.x & 63;
+    kchunk = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int row = (w * L + i) * 8 + (lane >> 3);
+      voff[i] = (int)(row * K) + kchunk * 16;
+    }
+  }
+
+  __device__ __forceinline__ void load(const uint8_t* tile, int64_t k0) const {
+    const bool kin = k0 + kchunk * 16 < K;
+    const uint32_t base = lds_addr(tile) + (uint32_t)(w * L * 1024);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int off = kin ? voff[i] + (int)k0 : (int)records;
+      dma16(rsrc, base + i * 1024, off);
+    }
+  }
+};
+
+// MFMA operand of 16 rows starting at `row0` of a BK = 128 LDS tile.
+__device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ s, int row0) {
+  const int l = threadIdx.x & 63;
+  const int r = row0 + (l & 15), g = l >> 4;
+  const uint4 lo = *reinterpret_cast<const uint4*>(s + swz(r, g));
+  const uint4 hi = *reinterpret_cast<const uint4*>(s + swz(r, g + 4));
+  v8i o;
+  o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+  o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+  return o;
+}
+
+template <int FA_OP, int FB_OP>
+__device__ __forceinline__ v4f mfma(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA_OP, FB_OP, 0, 0, 0, 0);
+}
+template <int FA_OP, int FB_OP>
+__device__ __forceinline__ v4f mfma_mx(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA_OP, FB_OP, 0, sa, 0, sb);
+}
+
+// Tile order: consecutive workgroups land on different XCDs (round robin over
+// 8), so workgroup b is first mapped to a contiguous range of tiles per XCD,
+// then tiles are walked in groups of 8 tile-rows so that neighbours share
+// A rows and B rows in that XCD's L2.
+__device__ __forceinline__ bool tile_coords(const Args& p, int& tm, int& tn) {
+  const int T = p.tiles_m * p.tiles_n;
+  const int per = (T + 7) / 8;
+  const int b = blockIdx.x;
+  const int t = (b & 7) * per + (b >> 3);
+  if (t >= T) return false;
+  constexpr int G = 8;
+  const int group = t / (G * p.tiles_n);
+  const int first_m = group * G;
+  const int gsize = min(p.tiles_m - first_m, G);
+  const int in_group = t - group * G * p.tiles_n;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+  return true;
+}
+
+// Workgroups for T tiles: a multiple of 8 so every XCD gets the same count.
+inline int grid_for_tiles(int T) { return ((T + 7) / 8) * 8; }
+
+}  // namespace
+}  // namespace fp8sg

@@ -36,5 +36,6 @@ struct GemmProblem {
   int bra, brb;
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_mx_k32(const GemmProblem& p, hipStream_t s);
 
 }  // namespace fp8sg

@@ -106,6 +106,7 @@ def test_gemm_errors(L):
     assert g(r(_op(0, 1)), r(_op(0, 2)), 16, 128, 64, P, None) == SHAPE   # K % 128
     assert g(r(_op(0, 1)), r(_op(0, 2)), 16, 100, 128, P, None) == SHAPE  # 128x128 rows
     assert g(r(_op(0, 3)), r(_op(0, 3)), 16, 16, 48, P, None) == SHAPE    # K % 32
+    assert g(r(t), r(t), 16, 16, (1 << 23) + 16, P, None) == SHAPE        # K > 2^23
     assert g(r(t), r(t), 16, 16, 16, PU, None) == ALIGN
     assert g(r(_op(0, 0, data=PU)), r(t), 16, 16, 16, P, None) == ALIGN
     # dgrad contracts over N, wgrad over M
