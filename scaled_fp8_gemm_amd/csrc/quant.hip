@@ -148,12 +148,22 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
 
 // Per-tensor cast with the transposed copy.  The tensor is cut into tiles of
 // 128 rows x 128 columns, visited grid-stride (tile t: row tile t / ntx,
-// column tile t % ntx); in a tile, thread (tr, tc) = (t / 16, t % 16) owns the
-// 8x8 sub-block at rows 8*tr.., columns 8*tc..  Loads: 16 lanes read 256
-// contiguous bytes of a row.  q rows are written 8 bytes per lane (128
-// contiguous bytes per 16 lanes); the 8x8 byte block is transposed in
-// registers and written to qT as 8 bytes per column.  Requires cols % 16 == 0
-// and rows % 16 == 0 (so row groups of 8 are never split by the edge).
+// column tile t % ntx).  In a tile, thread t owns rows 4a .. 4a+3 (a = t / 8)
+// and columns 16c .. 16c+15 (c = t % 8):
+//   1. two 16-byte loads per row (8 lanes read a row's 256 bytes), the cast,
+//      and one 16-byte q store per row (8 lanes write its 128 bytes);
+//   2. each 4x4 byte block is transposed in registers, giving for each of the
+//      thread's 16 columns the word of rows 4a .. 4a+3, which goes to an LDS
+//      copy of the qT tile (128 columns x 32 words, word a of column col at
+//      col*32 + (a ^ 4*((col >> 4) & 7)): two lanes per bank at most);
+//   3. after a barrier, thread t reads 16 bytes (words 4k .. 4k+3, k = t % 8)
+//      of qT rows (t / 8) + 32p, p = 0..3, and stores them: 8 lanes write a
+//      qT row's 128 bytes.
+// The LDS tile is double-buffered, so one barrier per tile suffices.
+// Requires cols % 16 == 0 and rows % 16 == 0 (edge tiles then hold whole
+// 16-row / 16-column groups).
+__device__ __forceinline__ int qt_word(int col, int a) { return col * 32 + (a ^ (((col >> 4) & 7) << 2)); }
+
 template <int FMT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict__ x, int64_t rows,
                                                      int64_t cols, int64_t ntx, int64_t ntiles,
@@ -162,32 +172,54 @@ __global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict_
                                                      uint8_t* __restrict__ qT,
                                                      uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
   const float s = *scale_p;
-  const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
+  const int t = threadIdx.x;
+  const int a = t >> 3, c = t & 7;
   uint32_t m = 0;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t r0 = (t / ntx) * 128 + tr * 8;
-    const int64_t c0 = (t % ntx) * 128 + tc * 8;
-    if (r0 >= rows || c0 >= cols) continue;
-    uint32_t lo[8], hi[8];
+  int buf = 0;
+  for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x, buf ^= 1) {
+    const int64_t r0 = (tt / ntx) * 128, c0 = (tt % ntx) * 128;
+    const int rv = (int)min<int64_t>(128, rows - r0), cv = (int)min<int64_t>(128, cols - c0);
+    uint32_t* T = tile[buf];
+    uint32_t b[4][4];   // [row i][word k] = columns 16c + 4k .. +3 of row 4a + i
+    if (4 * a < rv && 16 * c < cv) {
+      uint4 v[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = ld_stream((x + (r0 + i) * cols + c0));
-      if (AMAX) m = max(m, absmax8(v));
-      uint2 b = cast8<FMT>(v, s);
-      lo[i] = b.x;
-      hi[i] = b.y;
-      *(uint2*)(q + (r0 + i) * cols + c0) = b;
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* src = x + (r0 + 4 * a + i) * cols + c0 + 16 * c;
+        v[i][0] = ld_stream(src);
+        v[i][1] = ld_stream(src + 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (AMAX) m = max(m, max(absmax8(v[i][0]), absmax8(v[i][1])));
+        const uint2 lo = cast8<FMT>(v[i][0], s), hi = cast8<FMT>(v[i][1], s);
+        b[i][0] = lo.x; b[i][1] = lo.y; b[i][2] = hi.x; b[i][3] = hi.y;
+        *reinterpret_cast<uint4*>(q + (r0 + 4 * a + i) * cols + c0 + 16 * c) =
+            make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b[i][k] = 0;
     }
-    uint32_t tl[4], th[4], bl[4], bh[4];
-    transpose4x4(lo[0], lo[1], lo[2], lo[3], tl);   // columns 0-3, rows 0-3
-    transpose4x4(lo[4], lo[5], lo[6], lo[7], bl);   // columns 0-3, rows 4-7
-    transpose4x4(hi[0], hi[1], hi[2], hi[3], th);   // columns 4-7, rows 0-3
-    transpose4x4(hi[4], hi[5], hi[6], hi[7], bh);   // columns 4-7, rows 4-7
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *(uint2*)(qT + (c0 + j) * rows + r0) = make_uint2(tl[j], bl[j]);
-      *(uint2*)(qT + (c0 + 4 + j) * rows + r0) = make_uint2(th[j], bh[j]);
+    for (int k = 0; k < 4; ++k) {
+      uint32_t col4[4];
+      transpose4x4(b[0][k], b[1][k], b[2][k], b[3][k], col4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T[qt_word(16 * c + 4 * k + i, a)] = col4[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int col = (t >> 3) + 32 * p, k = t & 7;
+      if (col < cv && 16 * k < rv) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&T[qt_word(col, 4 * k)]);
+        *reinterpret_cast<uint4*>(qT + (c0 + col) * rows + r0 + 16 * k) = w;
+      }
     }
   }
   if (AMAX) {
