@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=list(SLUG))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
@@ -53,8 +53,12 @@ def parse():
 
 COPY_BYTES = 512 << 20
 # file-name slug of each workload (profiles/ summaries are named by kernel + slug)
+# (c3-step / c5-step: the blockwise and MXFP8 training steps -- fprop, dgrad,
+# wgrad with column-wise transposed copies -- at the QKV and GPT-175B shapes)
 SLUG = {"c2": "llama7b_upproj_4096x4096x11008", "c3": "qkv_block_8192x4096x12288",
-        "c4": "llama13b_step_8192x5120x13824", "c5": "gpt175b_mlp_mx_4096x12288x49152"}
+        "c4": "llama13b_step_8192x5120x13824", "c5": "gpt175b_mlp_mx_4096x12288x49152",
+        "c3-step": "qkv_block_step_8192x4096x12288",
+        "c5-step": "gpt175b_mlp_mx_step_4096x12288x49152"}
 # sources of the GEMM kernel the traffic counters describe
 GEMM_SOURCES = [os.path.join(ROOT, "scaled_fp8_gemm_amd", "csrc", f)
                 for f in ("gemm.hip", "gemm_common.h", "fp8_device.h")]
@@ -110,8 +114,11 @@ class Path:
         from scaled_fp8_gemm_amd import fp8sg as F
         from scaled_fp8_gemm_amd import gen
         self.F, self.torch, self.key = F, torch, key
-        cfg = gen.CONFIGS[key]
+        cfg = gen.CONFIGS[key.split("-")[0]]
         self.cfg = cfg
+        # the recipe of one step: the config's own, or its training step
+        self.kind = cfg.recipe if "-" not in key else {"block": "block-step",
+                                                       "mx": "mx-step"}[cfg.recipe]
         M, K, N = cfg.M, cfg.K, cfg.N
         self.M, self.K, self.N = M, K, N
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
@@ -120,7 +127,23 @@ class Path:
         self.xq, self.wq = e((M, K), torch.uint8), e((N, K), torch.uint8)
         self.y = e((M, N), torch.bfloat16)
         f1 = lambda: e(1, torch.float32)
-        if cfg.recipe == "tensor":
+        if self.kind in ("block-step", "mx-step"):
+            self.g = gen.make_g(cfg, dev)
+            self.xqT, self.wqT = e((K, M), torch.uint8), e((K, N), torch.uint8)
+            self.gq, self.gqT = e((M, N), torch.uint8), e((N, M), torch.uint8)
+            self.dx, self.dw = e((M, K), torch.bfloat16), e((N, K), torch.bfloat16)
+            self.flops = 3 * 2.0 * M * N * K
+            if self.kind == "block-step":
+                f32 = torch.float32
+                self.xs, self.xsT = e((M, K // 128), f32), e((K, M // 128), f32)
+                self.ws, self.wsT = e((N // 128, K // 128), f32), e((K // 128, N // 128), f32)
+                self.gs, self.gsT = e((M, N // 128), f32), e((N, M // 128), f32)
+            else:
+                u8 = torch.uint8
+                self.xs, self.xsT = e((M, K // 32), u8), e((K, M // 32), u8)
+                self.ws, self.wsT = e((N, K // 32), u8), e((K, N // 32), u8)
+                self.gs, self.gsT = e((M, N // 32), u8), e((N, M // 32), u8)
+        elif cfg.recipe == "tensor":
             self.xa, self.xs, self.xsi = f1(), f1(), f1()
             self.wa, self.ws, self.wsi = f1(), f1(), f1()
             self.flops = 2.0 * M * N * K
@@ -153,8 +176,33 @@ class Path:
         M, K, N = self.M, self.K, self.N
         c = lambda label, kind, work, fn, *a: self._call(record, label, kind, work, fn, *a)
         gemm = 2.0 * M * N * K
-        r = self.cfg.recipe
-        if r == "tensor":
+        r = self.kind
+        if r in ("block-step", "mx-step"):
+            blk = r == "block-step"
+            E4 = F.E4M3
+            if blk:
+                sx, sw = F.SCALE_BLOCK_1x128, F.SCALE_BLOCK_128x128
+                qt = lambda label, t, br, *out: c(
+                    label, "hbm", 4 * t.numel() + 8 * t.numel() // (128 * br),
+                    F.fp8_quantize_block_t, t, E4, br, *out)
+                qt("block_t X", self.x, 1, self.xq, self.xs, self.xqT, self.xsT)
+                qt("block_t W", self.w, 128, self.wq, self.ws, self.wqT, self.wsT)
+                qt("block_t G", self.g, 1, self.gq, self.gs, self.gqT, self.gsT)
+            else:
+                sx = sw = F.SCALE_MX_1x32
+                qt = lambda label, t, *out: c(label, "hbm", 4 * t.numel() + 2 * t.numel() // 32,
+                                              F.fp8_quantize_mx_t, t, E4, *out)
+                qt("mx_t X", self.x, self.xq, self.xs, self.xqT, self.xsT)
+                qt("mx_t W", self.w, self.wq, self.ws, self.wqT, self.wsT)
+                qt("mx_t G", self.g, self.gq, self.gs, self.gqT, self.gsT)
+            sg = sx
+            c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop, F.operand(self.xq, E4, sx, self.xs),
+              F.operand(self.wq, E4, sw, self.ws), M, N, K, self.y)
+            c("gemm dgrad", "mfma", gemm, F.fp8_gemm_dgrad, F.operand(self.gq, E4, sg, self.gs),
+              F.operand(self.wqT, E4, sw, self.wsT), M, N, K, self.dx)
+            c("gemm wgrad", "mfma", gemm, F.fp8_gemm_wgrad, F.operand(self.gqT, E4, sg, self.gsT),
+              F.operand(self.xqT, E4, sx, self.xsT), M, N, K, self.dw)
+        elif r == "tensor":
             c("amax X", "hbm", 2 * M * K, F.fp8_amax, self.x, F.E4M3, self.xa, self.xs, self.xsi)
             c("amax W", "hbm", 2 * N * K, F.fp8_amax, self.w, F.E4M3, self.wa, self.ws, self.wsi)
             c("cast X", "hbm", 3 * M * K, F.fp8_quantize_tensor, self.x, F.E4M3, self.xs, self.xq)
@@ -304,11 +352,18 @@ def main():
     recipe = {"tensor": "per-tensor current scaling, E4M3 x E4M3",
               "block": "blockwise 1x128 (X) / 128x128 (W), E4M3",
               "delayed": "delayed scaling H=16, fprop+dgrad+wgrad, E4M3 / E5M2 grads",
-              "mx": "MXFP8 1x32 E8M0, E4M3"}[cfg.recipe]
+              "mx": "MXFP8 1x32 E8M0, E4M3",
+              "block-step": "blockwise training step: X, G 1x128 (+ column-wise 128-token "
+                            "tiles for wgrad), W 128x128 (+ W^T), fprop+dgrad+wgrad, E4M3",
+              "mx-step": "MXFP8 training step: 1x32 E8M0 blocks along each GEMM's "
+                         "contraction (row- and column-wise copies), fprop+dgrad+wgrad, "
+                         "E4M3"}[p.kind]
     kernel = {"tensor": "k_gemm8<tensor> (FP8 MFMA 16x16x128, 8 waves, 256x256 tile)",
               "block": "k_gemm8<block> (FP8 MFMA, per-128-K promotion on VALU)",
               "delayed": "k_gemm8<tensor> (fprop, dgrad, wgrad launches)",
-              "mx": "k_gemm8<mx> (block-scaled MFMA 16x16x128, E8M0 operands)"}[cfg.recipe]
+              "mx": "k_gemm8<mx> (block-scaled MFMA 16x16x128, E8M0 operands)",
+              "block-step": "k_gemm8<block> (fprop, dgrad, wgrad launches)",
+              "mx-step": "k_gemm8<mx> (fprop, dgrad, wgrad launches)"}[p.kind]
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -323,7 +378,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N, "recipe": recipe},
+        "config": {"workload": cfg.name if p.kind == cfg.recipe else
+                   f"{cfg.name.split(',')[0]}, training step",
+                   "M": cfg.M, "K": cfg.K, "N": cfg.N, "recipe": recipe},
         "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),

@@ -154,6 +154,45 @@ fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, 
 fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                              uint8_t* q, uint8_t* scale_e8m0, void* stream);
 
+/* Blockwise cast with a transposed, column-wise copy for the backward GEMMs.
+ * [guide] blockwise scaling: inputs and gradients in 1x128 tiles, weights in
+ * 128x128 blocks.  dgrad contracts over the output features and wgrad over
+ * the tokens, so next to the row-wise copy of a tensor x they need the
+ * quantisation of x^T (W^T for dgrad, G^T and X^T for wgrad), whose
+ * 128-long tiles run along x's rows:
+ *   block_rows = 1    q, scale_inv   as fp8_quantize_block(x, 1, 128)
+ *                     qT, scale_inv_T as fp8_quantize_block(x^T, 1, 128):
+ *                     each column of x is cut into 128-row tiles, each tile
+ *                     scaled on its own (re-quantised from BF16)
+ *   block_rows = 128  q, scale_inv   as fp8_quantize_block(x, 128, 128)
+ *                     qT = q^T, scale_inv_T = scale_inv^T (same blocks)
+ *   x_bf16       [rows][cols] BF16, rows % 128 == 0, cols % 128 == 0
+ *   q            out uint8 [rows][cols], nullable (then scale_inv NULL too)
+ *   scale_inv    out float [rows/block_rows][cols/128]
+ *   qT           out uint8 [cols][rows]
+ *   scale_inv_T  out float [cols][rows/128] (block_rows 1) or
+ *                [cols/128][rows/128] (block_rows 128)
+ * One read of x writes both copies.  Errors: NULL (or q / scale_inv not both
+ * given); sizes; block shape; alignment; fmt. */
+fp8_status_t fp8_quantize_block_t(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                  int32_t block_rows, uint8_t* q, float* scale_inv, uint8_t* qT,
+                                  float* scale_inv_T, void* stream);
+
+/* MX cast with a transposed, column-wise copy for the backward GEMMs
+ * ([guide] MXFP8 scaling: 1x32 blocks, E8M0 scales):
+ *   q, scale_e8m0      as fp8_quantize_mx(x)   (blocks along x's rows)
+ *   qT, scale_e8m0_T   as fp8_quantize_mx(x^T) (each column of x cut into
+ *                      32-row blocks, re-quantised from BF16)
+ *   x_bf16        [rows][cols] BF16, rows % 32 == 0, cols % 32 == 0
+ *   q             out uint8 [rows][cols], nullable (then scale_e8m0 NULL too)
+ *   scale_e8m0    out uint8 [rows][cols/32]
+ *   qT            out uint8 [cols][rows]
+ *   scale_e8m0_T  out uint8 [cols][rows/32]
+ * Errors: NULL (or q / scale_e8m0 not both given); sizes; alignment; fmt. */
+fp8_status_t fp8_quantize_mx_t(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                               uint8_t* q, uint8_t* scale_e8m0, uint8_t* qT,
+                               uint8_t* scale_e8m0_T, void* stream);
+
 /* The three GEMMs of a linear layer ([guide] code changes; [snippets] forward
  * and backward flow), FP32 accumulation on MFMA, BF16 output (round to nearest
  * even).  Both operands are K-contiguous ("TN"), so one kernel serves all three:

@@ -140,6 +140,37 @@ fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, 
                                           st(stream)));
 }
 
+fp8_status_t fp8_quantize_block_t(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                                  int32_t block_rows, uint8_t* q, float* scale_inv, uint8_t* qT,
+                                  float* scale_inv_T, void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (!have(x_bf16, n) || !have(qT, n) || !have(scale_inv_T, n)) return FP8_ERR_NULL;
+  if ((q == nullptr) != (scale_inv == nullptr)) return FP8_ERR_NULL;
+  if (block_rows != 1 && block_rows != 128) return FP8_ERR_UNSUPPORTED;
+  if (rows % 128 || cols % 128) return FP8_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(qT, 16) || !aligned(scale_inv_T, 4) ||
+      (q && (!aligned(q, 16) || !aligned(scale_inv, 4))))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_t(x_bf16, rows, cols, fmt, block_rows == 1 ? 0 : 1, q,
+                                      scale_inv, qT, scale_inv_T, st(stream)));
+}
+
+fp8_status_t fp8_quantize_mx_t(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
+                               uint8_t* q, uint8_t* scale_e8m0, uint8_t* qT,
+                               uint8_t* scale_e8m0_T, void* stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (!have(x_bf16, n) || !have(qT, n) || !have(scale_e8m0_T, n)) return FP8_ERR_NULL;
+  if ((q == nullptr) != (scale_e8m0 == nullptr)) return FP8_ERR_NULL;
+  if (rows % 32 || cols % 32) return FP8_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(qT, 16) || (q && !aligned(q, 16))) return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_t(x_bf16, rows, cols, fmt, 2, q, scale_e8m0, qT,
+                                      scale_e8m0_T, st(stream)));
+}
+
 fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                              uint8_t* q, uint8_t* scale_e8m0, void* stream) {
   if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;

@@ -20,6 +20,10 @@ hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int 
                                  uint8_t* q, float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt, uint8_t* q,
                               uint8_t* e8m0, hipStream_t s);
+// Row-wise copy (optional) and transposed column-wise copy; kind 0: 1x128
+// blocks, 1: 128x128 blocks, 2: MX 1x32 blocks.
+hipError_t launch_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt, int kind,
+                             uint8_t* q, void* sq, uint8_t* qT, void* sqT, hipStream_t s);
 hipError_t launch_convert(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s);
 
 // C[M][N] (BF16) = A[M][K] . B[N][K]^T with the operands' scales.

@@ -330,14 +330,13 @@ __device__ __forceinline__ int mx_exponent_bits(uint32_t abits) {
   return min(127, max(-127, e));
 }
 
-// One 32-element block held by 4 lanes (one 16-byte load each).
+// Scale 2^-e of an MX block from its BF16 magnitude bits m, and the E8M0
+// byte: inf/NaN in the block -> 0xFF (elements cast unscaled), all-zero ->
+// 127, else e from mx_exponent_bits.
 template <int FMT>
-__device__ __forceinline__ void mx_block(uint4 v, int64_t b, int sub, uint2* __restrict__ q,
-                                         uint8_t* __restrict__ e8m0) {
-  const uint32_t m = group_max_u32<4>(absmax8(v));   // BF16 magnitude bits
+__device__ __forceinline__ float mx_scale(uint32_t m, uint32_t& byte) {
   int e;
-  uint32_t byte;
-  if (m >= 0x7f80u) {            // inf or NaN in the block
+  if (m >= 0x7f80u) {
     e = 0;
     byte = 0xffu;
   } else if (m == 0u) {
@@ -347,7 +346,15 @@ __device__ __forceinline__ void mx_block(uint4 v, int64_t b, int sub, uint2* __r
     e = mx_exponent_bits<FMT>(m << 16);
     byte = (uint32_t)(e + 127);
   }
-  const float s = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 120]
+  return __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 120]
+}
+
+// One 32-element block held by 4 lanes (one 16-byte load each).
+template <int FMT>
+__device__ __forceinline__ void mx_block(uint4 v, int64_t b, int sub, uint2* __restrict__ q,
+                                         uint8_t* __restrict__ e8m0) {
+  uint32_t byte;
+  const float s = mx_scale<FMT>(group_max_u32<4>(absmax8(v)), byte);
   q[b * 4 + sub] = cast8<FMT>(v, s);
   if (sub == 0) e8m0[b] = (uint8_t)byte;
 }
@@ -371,6 +378,183 @@ __global__ __launch_bounds__(kThreads) void k_mx(const uint4* __restrict__ x, in
       for (int u = 0; u < U; ++u)
         if (b + u * G < nblocks)
           mx_block<FMT>(ld_stream(&x[(b + u * G) * 4 + sub]), b + u * G, sub, q, e8m0);
+    }
+  }
+}
+
+// Quantise with a transposed, column-wise copy, for the backward GEMMs
+// (guide, "blockwise scaling": gradients and inputs in 1x128 tiles, weights
+// in 128x128 blocks; "MXFP8 scaling": 1x32 blocks).  dgrad contracts over the
+// output features and wgrad over the tokens, so besides the row-wise copy
+// (q, blocks along the columns) they need qT = the quantisation of x^T, whose
+// blocks run along x's rows:
+//   kTBlock1   q: 1x128 blocks per row; qT: per column, 128-row blocks
+//   kTBlock128 one scale per 128x128 block; qT is the transpose of q
+//   kTMX       q: 1x32 E8M0 blocks per row; qT: per column, 32-row blocks
+// A 256-thread workgroup handles a 128 x 128 tile as k_cast_t does (thread t:
+// rows 4a .. 4a+3, a = t / 8, columns 16c .. 16c+15, c = t % 8): row maxima
+// reduce over the 8 lanes of a row (1x128) or 2 lanes (1x32); column maxima
+// over the thread's 4 rows, then over the 8 lanes of a column in the wave
+// (32 rows: one MX block), then across the 4 waves through LDS (128 rows).
+// The column-scaled bytes go through the LDS transpose of k_cast_t.
+enum : int { kTBlock1 = 0, kTBlock128 = 1, kTMX = 2 };
+
+// Element j (0..15) of a thread's row held as two 16-byte loads.
+__device__ __forceinline__ float row_elem(const uint4 (&v)[2], int j) {
+  const uint4 h = v[j >> 3];
+  const int wd = (j & 7) >> 1;
+  const uint32_t w = wd == 0 ? h.x : wd == 1 ? h.y : wd == 2 ? h.z : h.w;
+  return (j & 1) ? bf_hi(w) : bf_lo(w);
+}
+__device__ __forceinline__ uint32_t row_mag(const uint4 (&v)[2], int j) {
+  const uint4 h = v[j >> 3];
+  const int wd = (j & 7) >> 1;
+  const uint32_t w = wd == 0 ? h.x : wd == 1 ? h.y : wd == 2 ? h.z : h.w;
+  return ((j & 1) ? (w >> 16) : w) & 0x7fffu;
+}
+
+template <int FMT, int KIND>
+__global__ __launch_bounds__(kThreads) void k_quant_t(const uint16_t* __restrict__ x,
+                                                      int64_t rows, int64_t cols, int64_t ntx,
+                                                      int64_t ntiles, uint8_t* __restrict__ q,
+                                                      void* __restrict__ sq,
+                                                      uint8_t* __restrict__ qT,
+                                                      void* __restrict__ sqT) {
+  constexpr int RB = KIND == kTMX ? 32 : 128;   // block length along a row / a column
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
+  __shared__ __attribute__((aligned(16))) uint32_t cmax[KIND == kTBlock1 ? 2 : 1][4][128];
+  const int t = threadIdx.x;
+  const int a = t >> 3, c = t & 7, w = t >> 6, lane = t & 63;
+  const int64_t row_blocks = cols / RB, col_blocks = rows / RB;
+  int buf = 0;
+  for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x, buf ^= 1) {
+    const int64_t r0 = (tt / ntx) * 128, c0 = (tt % ntx) * 128;
+    const int rv = (int)min<int64_t>(128, rows - r0), cv = (int)min<int64_t>(128, cols - c0);
+    const bool valid = 4 * a < rv && 16 * c < cv;
+    uint4 v[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (valid) {
+        const uint16_t* src = x + (r0 + 4 * a + i) * cols + c0 + 16 * c;
+        v[i][0] = ld_stream(src);
+        v[i][1] = ld_stream(src + 8);
+      } else {
+        v[i][0] = v[i][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    uint32_t rm[4], cm[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rm[i] = max(absmax8(v[i][0]), absmax8(v[i][1]));
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      cm[j] = max(max(row_mag(v[0], j), row_mag(v[1], j)), max(row_mag(v[2], j), row_mag(v[3], j)));
+
+    // ---- row-wise copy
+    float st = 1.0f;   // kTBlock128: the tile's scale (rows and columns alike)
+    if constexpr (KIND == kTBlock128) {
+      const uint32_t m = block_max_u32<kThreads>(max(max(rm[0], rm[1]), max(rm[2], rm[3])), red);
+      st = scale_from_amax<FMT>(__uint_as_float(m << 16));
+    }
+    if (q != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sr;
+        uint32_t byte = 0;
+        if constexpr (KIND == kTBlock1) sr = scale_from_amax<FMT>(__uint_as_float(group_max_u32<8>(rm[i]) << 16));
+        else if constexpr (KIND == kTMX) sr = mx_scale<FMT>(group_max_u32<2>(rm[i]), byte);
+        else sr = st;
+        if (valid) {
+          const uint2 lo = cast8<FMT>(v[i][0], sr), hi = cast8<FMT>(v[i][1], sr);
+          const int64_t row = r0 + 4 * a + i;
+          *reinterpret_cast<uint4*>(q + row * cols + c0 + 16 * c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          if constexpr (KIND == kTBlock1) {
+            if (c == 0) static_cast<float*>(sq)[row * row_blocks + c0 / 128] = 1.0f / sr;
+          } else if constexpr (KIND == kTMX) {
+            if ((c & 1) == 0) static_cast<uint8_t*>(sq)[row * row_blocks + (c0 + 16 * c) / 32] = (uint8_t)byte;
+          }
+        }
+      }
+      if constexpr (KIND == kTBlock128)
+        if (t == 0) static_cast<float*>(sq)[(r0 / 128) * row_blocks + c0 / 128] = 1.0f / st;
+    }
+
+    // ---- column scales
+    float sc[16];
+    uint32_t cbyte[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (KIND == kTBlock128) {
+        sc[j] = st;
+      } else {
+        uint32_t m = cm[j];
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        if constexpr (KIND == kTMX) {
+          sc[j] = mx_scale<FMT>(m, cbyte[j]);
+        } else {
+          cm[j] = m;   // this wave's 32 rows
+        }
+      }
+    }
+    if constexpr (KIND == kTBlock1) {
+      if (lane < 8) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 4)
+          *reinterpret_cast<uint4*>(&cmax[buf][w][16 * c + j]) = make_uint4(cm[j], cm[j + 1], cm[j + 2], cm[j + 3]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        uint4 m4 = *reinterpret_cast<const uint4*>(&cmax[buf][0][16 * c + j]);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+          const uint4 o = *reinterpret_cast<const uint4*>(&cmax[buf][ww][16 * c + j]);
+          m4.x = max(m4.x, o.x); m4.y = max(m4.y, o.y); m4.z = max(m4.z, o.z); m4.w = max(m4.w, o.w);
+        }
+        sc[j] = scale_from_amax<FMT>(__uint_as_float(m4.x << 16));
+        sc[j + 1] = scale_from_amax<FMT>(__uint_as_float(m4.y << 16));
+        sc[j + 2] = scale_from_amax<FMT>(__uint_as_float(m4.z << 16));
+        sc[j + 3] = scale_from_amax<FMT>(__uint_as_float(m4.w << 16));
+      }
+    }
+
+    // ---- column-wise copy: scale, cast, transpose through LDS, qT stores
+    uint32_t* T = tile[buf];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        b[i] = cvt4<FMT>(row_elem(v[i], 4 * k) * sc[4 * k], row_elem(v[i], 4 * k + 1) * sc[4 * k + 1],
+                         row_elem(v[i], 4 * k + 2) * sc[4 * k + 2], row_elem(v[i], 4 * k + 3) * sc[4 * k + 3]);
+      uint32_t col4[4];
+      transpose4x4(b[0], b[1], b[2], b[3], col4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T[qt_word(16 * c + 4 * k + i, a)] = col4[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int col = (t >> 3) + 32 * p, k = t & 7;
+      if (col < cv && 16 * k < rv) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(&T[qt_word(col, 4 * k)]);
+        *reinterpret_cast<uint4*>(qT + (c0 + col) * rows + r0 + 16 * k) = wv;
+      }
+    }
+    // column scales of the transposed copy
+    if constexpr (KIND == kTBlock1) {
+      if (t < 8)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          static_cast<float*>(sqT)[(c0 + 16 * c + j) * col_blocks + r0 / 128] = 1.0f / sc[j];
+    } else if constexpr (KIND == kTMX) {
+      if (lane < 8 && 32 * w < rv && 16 * c < cv)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          static_cast<uint8_t*>(sqT)[(c0 + 16 * c + j) * col_blocks + r0 / 32 + w] = (uint8_t)cbyte[j];
+    } else {
+      if (t == 0) static_cast<float*>(sqT)[(c0 / 128) * col_blocks + r0 / 128] = 1.0f / st;
     }
   }
 }
@@ -554,6 +738,27 @@ hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt
   FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_mx<F>, dim3(g), dim3(kThreads), 0, s,
                                              static_cast<const uint4*>(x), nblocks,
                                              reinterpret_cast<uint2*>(q), e8m0));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt, int kind,
+                             uint8_t* q, void* sq, uint8_t* qT, void* sqT, hipStream_t s) {
+  if (rows * cols == 0) return hipSuccess;
+  const int64_t ntx = (cols + 127) / 128;
+  const int64_t ntiles = ntx * ((rows + 127) / 128);
+  const int g = grid_for(ntiles, 1);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  FP8SG_FMT_DISPATCH(fmt, {
+    if (kind == kTBlock1)
+      hipLaunchKernelGGL((k_quant_t<F, kTBlock1>), dim3(g), dim3(kThreads), 0, s, xp, rows, cols,
+                         ntx, ntiles, q, sq, qT, sqT);
+    else if (kind == kTBlock128)
+      hipLaunchKernelGGL((k_quant_t<F, kTBlock128>), dim3(g), dim3(kThreads), 0, s, xp, rows,
+                         cols, ntx, ntiles, q, sq, qT, sqT);
+    else
+      hipLaunchKernelGGL((k_quant_t<F, kTMX>), dim3(g), dim3(kThreads), 0, s, xp, rows, cols, ntx,
+                         ntiles, q, sq, qT, sqT);
+  });
   return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ class Operand(ctypes.Structure):
 
 _lib = None
 _EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_amax_history_update", "fp8_quantize_block",
-            "fp8_quantize_mx", "fp8_gemm_fprop", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
-            "fp8_convert_f32", "fp8_status_string"]
+            "fp8_quantize_mx", "fp8_quantize_block_t", "fp8_quantize_mx_t", "fp8_gemm_fprop",
+            "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_convert_f32", "fp8_status_string"]
 
 
 def lib():
@@ -58,6 +58,8 @@ def lib():
             "fp8_amax_history_update": [vp, i32, i64, vp, i32, vp, vp, vp],
             "fp8_quantize_block": [vp, i64, i64, i32, i32, i32, vp, vp, vp],
             "fp8_quantize_mx": [vp, i64, i64, i32, vp, vp, vp],
+            "fp8_quantize_block_t": [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp],
+            "fp8_quantize_mx_t": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_gemm_fprop": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_dgrad": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_wgrad": [vp, vp, i64, i64, i64, vp, vp],
@@ -123,6 +125,21 @@ def fp8_quantize_mx(x, fmt, q, scale_e8m0, stream=None):
     rows, cols = _rc(x)
     _check("fp8_quantize_mx", lib().fp8_quantize_mx(_ptr(x), rows, cols, fmt, _ptr(q),
                                                     _ptr(scale_e8m0), _stream(stream)))
+
+
+def fp8_quantize_block_t(x, fmt, block_rows, q, scale_inv, qT, scale_inv_T, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_quantize_block_t",
+           lib().fp8_quantize_block_t(_ptr(x), rows, cols, fmt, block_rows, _ptr(q),
+                                      _ptr(scale_inv), _ptr(qT), _ptr(scale_inv_T),
+                                      _stream(stream)))
+
+
+def fp8_quantize_mx_t(x, fmt, q, scale_e8m0, qT, scale_e8m0_T, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_quantize_mx_t",
+           lib().fp8_quantize_mx_t(_ptr(x), rows, cols, fmt, _ptr(q), _ptr(scale_e8m0), _ptr(qT),
+                                   _ptr(scale_e8m0_T), _stream(stream)))
 
 
 def operand(data, fmt, scaling, scale_inv) -> Operand:

@@ -206,7 +206,8 @@ def make_w(cfg: Config, device="cpu", N=None, K=None) -> torch.Tensor:
 
 
 def make_g(cfg: Config, device="cpu", step: int = 0, M=None, N=None) -> torch.Tensor:
-    """Output gradient dY[M, N] ~ N(0, 1e-3) (the training-step workload)."""
+    """Output gradient dY[M, N] ~ N(0, 1e-3), for the training steps of every
+    recipe (fresh per step)."""
     M = cfg.M if M is None else M
     N = cfg.N if N is None else N
     return normal_bf16((M, N), 1e-3, seed_for(cfg.key, "G", step), device)

@@ -84,6 +84,24 @@ def test_block_and_mx_errors(L):
     assert m(PU, 4, 64, 0, P, P, None) == ALIGN
 
 
+def test_transposed_block_and_mx_errors(L):
+    bt = L.fp8_quantize_block_t
+    assert bt(P, 128, 256, 0, 2, P, P, P, P, None) == UNSUP           # block_rows
+    assert bt(P, 100, 256, 0, 1, P, P, P, P, None) == SHAPE           # rows % 128
+    assert bt(P, 128, 200, 0, 128, P, P, P, P, None) == SHAPE         # cols % 128
+    assert bt(P, 128, 256, 0, 1, P, None, P, P, None) == NULL         # q without scale_inv
+    assert bt(P, 128, 256, 0, 1, None, None, None, P, None) == NULL   # qT required
+    assert bt(P, 128, 256, 0, 1, None, None, P, None, None) == NULL
+    assert bt(P, 128, 256, 0, 1, None, None, PU, P, None) == ALIGN
+    assert bt(P, 128, 256, 2, 1, None, None, P, P, None) == UNSUP     # fmt
+    mt = L.fp8_quantize_mx_t
+    assert mt(P, 48, 64, 0, P, P, P, P, None) == SHAPE                # rows % 32
+    assert mt(P, 64, 48, 0, P, P, P, P, None) == SHAPE                # cols % 32
+    assert mt(P, 64, 64, 0, None, P, P, P, None) == NULL
+    assert mt(P, 64, 64, 0, None, None, None, P, None) == NULL
+    assert mt(PU, 64, 64, 0, None, None, P, P, None) == ALIGN
+
+
 def _op(fmt, scaling, data=P, s=P):
     from scaled_fp8_gemm_amd import fp8sg
     return fp8sg.Operand(data, fmt, scaling, s)

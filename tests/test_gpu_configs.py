@@ -192,3 +192,91 @@ def test_delayed_training_step_16(F, orc):
                                s["w"], f"step {t} dgrad", seed=t + 100)
             check_gemm_sampled(orc, dw, host["g"][1], host["x"][1], E5M2, E4M3, 0, s["g"],
                                s["x"], f"step {t} wgrad", seed=t + 200)
+
+
+def test_blockwise_training_step_qkv(F, orc):
+    """The blockwise recipe's training step at the QKV shape: X and G in 1x128
+    tiles with column-wise transposed copies (128-token tiles) for wgrad, W in
+    128x128 blocks with W^T for dgrad; every byte and scale bit-exact, GEMM
+    entries sampled."""
+    cfg = gen.CONFIGS["c3"]
+    M, K, N = cfg.M, cfg.K, cfg.N
+    out = {}
+    for name, make, br in (("x", gen.make_x, 1), ("w", gen.make_w, 128), ("g", gen.make_g, 1)):
+        t = make(cfg, DEV)
+        R, C = t.shape
+        q, qT = empty((R, C), torch.uint8), empty((C, R), torch.uint8)
+        s = empty((R // br, C // 128), torch.float32)
+        sT = empty((C, R // 128) if br == 1 else (C // 128, R // 128), torch.float32)
+        F.fp8_quantize_block_t(t, E4M3, br, q, s, qT, sT)
+        torch.cuda.synchronize()
+        tb = bits16(t)
+        del t
+        wq, ws = orc.quantize_block(tb, E4M3, br, 128)
+        if br == 1:
+            wqT, wsT = orc.quantize_block(np.ascontiguousarray(tb.T), E4M3, 1, 128)
+        else:
+            wqT, wsT = np.ascontiguousarray(wq.T), np.ascontiguousarray(ws.T)
+        del tb
+        for got, want, what in ((q, wq, "q"), (qT, wqT, "qT")):
+            assert np.array_equal(bytes8(got), want), f"{name} {what}"
+        for got, want, what in ((s, ws, "scale_inv"), (sT, wsT, "scale_inv_T")):
+            assert np.array_equal(f32(got).view(np.uint32), want.view(np.uint32)), f"{name} {what}"
+        out[name] = (q, s, qT, sT, wq, ws, wqT, wsT)
+    x, w, g = out["x"], out["w"], out["g"]
+    y, dx, dw = empty((M, N), torch.bfloat16), empty((M, K), torch.bfloat16), \
+        empty((N, K), torch.bfloat16)
+    F.fp8_gemm_fprop(F.operand(x[0], E4M3, B1, x[1]), F.operand(w[0], E4M3, B128, w[1]),
+                     M, N, K, y)
+    F.fp8_gemm_dgrad(F.operand(g[0], E4M3, B1, g[1]), F.operand(w[2], E4M3, B128, w[3]),
+                     M, N, K, dx)
+    F.fp8_gemm_wgrad(F.operand(g[2], E4M3, B1, g[3]), F.operand(x[2], E4M3, B1, x[3]),
+                     M, N, K, dw)
+    torch.cuda.synchronize()
+    check_gemm_sampled(orc, y, x[4], w[4], E4M3, E4M3, 1, x[5], w[5], "block fprop", 1, 128,
+                       seed=11)
+    check_gemm_sampled(orc, dx, g[4], w[6], E4M3, E4M3, 1, g[5], w[7], "block dgrad", 1, 128,
+                       seed=12)
+    check_gemm_sampled(orc, dw, g[6], x[6], E4M3, E4M3, 1, g[7], x[7], "block wgrad", 1, 1,
+                       seed=13)
+
+
+def test_mx_training_step_gpt175b_share(F, orc):
+    """The MXFP8 training step at one GPU's share of the GPT-175B MLP: 1x32
+    E8M0 blocks along each GEMM's contraction (row-wise copies and
+    column-wise transposed copies); bytes and scale bytes bit-exact, GEMM
+    entries sampled."""
+    cfg = gen.CONFIGS["c5"]
+    M, K, N = cfg.M, cfg.K, cfg.N
+    out = {}
+    for name, make in (("x", gen.make_x), ("w", gen.make_w), ("g", gen.make_g)):
+        t = make(cfg, DEV)
+        R, C = t.shape
+        q, qT = empty((R, C), torch.uint8), empty((C, R), torch.uint8)
+        e, eT = empty((R, C // 32), torch.uint8), empty((C, R // 32), torch.uint8)
+        F.fp8_quantize_mx_t(t, E4M3, q, e, qT, eT)
+        torch.cuda.synchronize()
+        tb = bits16(t)
+        del t
+        wq, we = orc.quantize_mx(tb, E4M3)
+        assert np.array_equal(bytes8(e), we) and np.array_equal(bytes8(q), wq), name
+        tbT = np.ascontiguousarray(tb.T)
+        del tb
+        wqT, weT = orc.quantize_mx(tbT, E4M3)
+        del tbT
+        assert np.array_equal(bytes8(eT), weT) and np.array_equal(bytes8(qT), wqT), f"{name} T"
+        out[name] = (q, e, qT, eT, wq, we, wqT, weT)
+        torch.cuda.empty_cache()
+    x, w, g = out["x"], out["w"], out["g"]
+    y, dx, dw = empty((M, N), torch.bfloat16), empty((M, K), torch.bfloat16), \
+        empty((N, K), torch.bfloat16)
+    F.fp8_gemm_fprop(F.operand(x[0], E4M3, MX, x[1]), F.operand(w[0], E4M3, MX, w[1]),
+                     M, N, K, y)
+    F.fp8_gemm_dgrad(F.operand(g[0], E4M3, MX, g[1]), F.operand(w[2], E4M3, MX, w[3]),
+                     M, N, K, dx)
+    F.fp8_gemm_wgrad(F.operand(g[2], E4M3, MX, g[3]), F.operand(x[2], E4M3, MX, x[3]),
+                     M, N, K, dw)
+    torch.cuda.synchronize()
+    check_gemm_sampled(orc, y, x[4], w[4], E4M3, E4M3, 2, x[5], w[5], "mx fprop", seed=21)
+    check_gemm_sampled(orc, dx, g[4], w[6], E4M3, E4M3, 2, g[5], w[7], "mx dgrad", seed=22)
+    check_gemm_sampled(orc, dw, g[6], x[6], E4M3, E4M3, 2, g[7], x[7], "mx wgrad", seed=23)

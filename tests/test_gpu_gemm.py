@@ -144,3 +144,73 @@ def test_layer_three_gemms(F, orc, M, K, N):
                realistic=True)
     check_gemm(orc, bits16(dw), bytes8(gqT), bytes8(xqT), E5M2, E4M3, 0, sg, sx, label="wgrad",
                realistic=True)
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 384, 512), (384, 256, 640)])
+def test_layer_three_gemms_blockwise(F, orc, M, K, N):
+    """Blockwise training step: X and G in 1x128 tiles (row-wise copies along
+    their contraction, column-wise transposed copies for wgrad), W in 128x128
+    blocks (and W^T for dgrad), all E4M3; fprop (1x128 x 128x128), dgrad
+    (1x128 x 128x128), wgrad (1x128 x 1x128) against the oracle."""
+    x = rand_bits((M, K), 31, 1.0)
+    w = rand_bits((N, K), 32, 0.02)
+    gr = rand_bits((M, N), 33, 1e-3)
+    q = {}
+    for name, t, br in (("x", x, 1), ("w", w, 128), ("g", gr, 1)):
+        R, C = t.shape
+        qd = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+        sd = torch.empty((R // br, C // 128), dtype=torch.float32, device=DEV)
+        qTd = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+        sTd = torch.empty((C, R // 128) if br == 1 else (C // 128, R // 128), dtype=torch.float32,
+                          device=DEV)
+        F.fp8_quantize_block_t(dev_bf16(t), E4M3, br, qd, sd, qTd, sTd)
+        q[name] = (qd, sd, qTd, sTd)
+    (xq, xs, xqT, xsT), (wq, ws, wqT, wsT), (gq, gs, gqT, gsT) = q["x"], q["w"], q["g"]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(F.operand(xq, E4M3, B1, xs), F.operand(wq, E4M3, B128, ws), M, N, K, y)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_dgrad(F.operand(gq, E4M3, B1, gs), F.operand(wqT, E4M3, B128, wsT), M, N, K, dx)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_wgrad(F.operand(gqT, E4M3, B1, gsT), F.operand(xqT, E4M3, B1, xsT), M, N, K, dw)
+    torch.cuda.synchronize()
+    h = lambda d: bytes8(d)
+    check_gemm(orc, bits16(y), h(xq), h(wq), E4M3, E4M3, 1, f32(xs), f32(ws), 1, 128,
+               label="block fprop", realistic=True)
+    check_gemm(orc, bits16(dx), h(gq), h(wqT), E4M3, E4M3, 1, f32(gs), f32(wsT), 1, 128,
+               label="block dgrad", realistic=True)
+    check_gemm(orc, bits16(dw), h(gqT), h(xqT), E4M3, E4M3, 1, f32(gsT), f32(xsT), 1, 1,
+               label="block wgrad", realistic=True)
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 384, 512), (320, 256, 384)])
+def test_layer_three_gemms_mx(F, orc, M, K, N):
+    """MXFP8 training step: 1x32 E8M0 blocks along each GEMM's contraction --
+    row-wise copies for fprop / dgrad's left operand, column-wise transposed
+    copies (32-token or 32-feature blocks) for W^T, G^T and X^T."""
+    x = rand_bits((M, K), 41, 1.0)
+    w = rand_bits((N, K), 42, 0.006)
+    gr = rand_bits((M, N), 43, 1e-3)
+    q = {}
+    for name, t in (("x", x), ("w", w), ("g", gr)):
+        R, C = t.shape
+        qd = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+        ed = torch.empty((R, C // 32), dtype=torch.uint8, device=DEV)
+        qTd = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+        eTd = torch.empty((C, R // 32), dtype=torch.uint8, device=DEV)
+        F.fp8_quantize_mx_t(dev_bf16(t), E4M3, qd, ed, qTd, eTd)
+        q[name] = (qd, ed, qTd, eTd)
+    (xq, xe, xqT, xeT), (wq, we, wqT, weT), (gq, ge, gqT, geT) = q["x"], q["w"], q["g"]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(F.operand(xq, E4M3, MX, xe), F.operand(wq, E4M3, MX, we), M, N, K, y)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_dgrad(F.operand(gq, E4M3, MX, ge), F.operand(wqT, E4M3, MX, weT), M, N, K, dx)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_wgrad(F.operand(gqT, E4M3, MX, geT), F.operand(xqT, E4M3, MX, xeT), M, N, K, dw)
+    torch.cuda.synchronize()
+    h = bytes8
+    check_gemm(orc, bits16(y), h(xq), h(wq), E4M3, E4M3, 2, h(xe), h(we), label="mx fprop",
+               realistic=True)
+    check_gemm(orc, bits16(dx), h(gq), h(wqT), E4M3, E4M3, 2, h(ge), h(weT), label="mx dgrad",
+               realistic=True)
+    check_gemm(orc, bits16(dw), h(gqT), h(xqT), E4M3, E4M3, 2, h(geT), h(xeT), label="mx wgrad",
+               realistic=True)

@@ -153,6 +153,86 @@ def test_quantize_mx(F, orc, shape, fmt):
     assert np.array_equal(bytes8(q), wq)
 
 
+def _specials_in_columns(x):
+    """An all-zero column tile, a NaN, a -inf and a largest-BF16 entry in the
+    first column tile, so column scales meet every special case."""
+    R, C = x.shape
+    x[:, 5] = 0
+    x[7, 9] = 0x7FC0
+    x[min(130, R - 1), 11 % C] = 0xFF80
+    x[3, 13 % C] = 0x7F7F
+
+
+# (4224, 8192): 2112 tiles of 128 x 128, more than the launch's workgroups
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 1024), (4224, 8192)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("rowwise", [True, False])
+def test_quantize_block_t_1x128(F, orc, shape, fmt, rowwise):
+    """Row-wise 1x128 copy and the column-wise copy of x^T (128-row tiles)."""
+    R, C = shape
+    x = rand_bits(shape, 17 + R, 1.0, specials=True)
+    _specials_in_columns(x)
+    xd = dev_bf16(x)
+    q = empty_dev(shape, torch.uint8) if rowwise else None
+    si = empty_dev((R, C // 128), torch.float32) if rowwise else None
+    qT = empty_dev((C, R), torch.uint8)
+    siT = empty_dev((C, R // 128), torch.float32)
+    F.fp8_quantize_block_t(xd, fmt, 1, q, si, qT, siT)
+    wqT, wsiT = orc.quantize_block(np.ascontiguousarray(x.T), fmt, 1, 128)
+    assert np.array_equal(f32(siT).view(np.uint32), wsiT.view(np.uint32))
+    assert np.array_equal(bytes8(qT), wqT)
+    if rowwise:
+        wq, wsi = orc.quantize_block(x, fmt, 1, 128)
+        assert np.array_equal(f32(si).view(np.uint32), wsi.view(np.uint32))
+        assert np.array_equal(bytes8(q), wq)
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (384, 256), (1280, 2304)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_block_t_128(F, orc, shape, fmt):
+    """128x128 blocks: the transposed copy is q^T with the transposed grid."""
+    R, C = shape
+    x = rand_bits(shape, 19 + R, 0.02, specials=True)
+    _specials_in_columns(x)
+    q = empty_dev(shape, torch.uint8)
+    si = empty_dev((R // 128, C // 128), torch.float32)
+    qT = empty_dev((C, R), torch.uint8)
+    siT = empty_dev((C // 128, R // 128), torch.float32)
+    F.fp8_quantize_block_t(dev_bf16(x), fmt, 128, q, si, qT, siT)
+    wq, wsi = orc.quantize_block(x, fmt, 128, 128)
+    assert np.array_equal(bytes8(q), wq)
+    assert np.array_equal(f32(si).view(np.uint32), wsi.view(np.uint32))
+    assert np.array_equal(bytes8(qT), np.ascontiguousarray(wq.T))
+    assert np.array_equal(f32(siT).view(np.uint32), np.ascontiguousarray(wsi.T).view(np.uint32))
+
+
+# ragged edge tiles (96 x 160, 160 x 96) and more tiles than workgroups
+@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (160, 96), (4224, 8224)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("rowwise", [True, False])
+def test_quantize_mx_t(F, orc, shape, fmt, rowwise):
+    """Row-wise 1x32 MX copy and the column-wise copy of x^T (32-row blocks)."""
+    R, C = shape
+    x = rand_bits(shape, 23 + R, 4.0, specials=True)
+    x[0:32, 1] = 0                                     # zero column block -> 127
+    x[2, 3] = 0x7FC0                                   # NaN -> 0xFF
+    x[0:32, 4] = 0x0001                                # subnormal block -> clamp -127
+    x[0:32, 6] = 0x7F7F                                # largest BF16 -> e = 120
+    x[5, 7] = 0xFF80                                   # -inf -> 0xFF
+    q = empty_dev(shape, torch.uint8) if rowwise else None
+    e = empty_dev((R, C // 32), torch.uint8) if rowwise else None
+    qT = empty_dev((C, R), torch.uint8)
+    eT = empty_dev((C, R // 32), torch.uint8)
+    F.fp8_quantize_mx_t(dev_bf16(x), fmt, q, e, qT, eT)
+    wqT, weT = orc.quantize_mx(np.ascontiguousarray(x.T), fmt)
+    assert np.array_equal(bytes8(eT), weT)
+    assert np.array_equal(bytes8(qT), wqT)
+    if rowwise:
+        wq, we = orc.quantize_mx(x, fmt)
+        assert np.array_equal(bytes8(e), we)
+        assert np.array_equal(bytes8(q), wq)
+
+
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_convert_every_fp32_pattern(F, orc, fmt):
     """The cast's rounding routine on all 2^32 FP32 inputs, in 2^28 chunks."""
