@@ -21,7 +21,7 @@
  * Conventions for every call
  *   Memory      Every pointer argument except `stream` is device memory owned by
  *               the caller.  Tensors are dense and row-major.  The calls that
- *               produce an amax (fp8_amax, fp8_quantize_tensor with amax_out)
+ *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out)
  *               reduce through an 8 KB buffer of partial maxima that the
  *               library allocates (hipMalloc) on the first such call on each
  *               (device, stream) pair and keeps until the process ends; calls
@@ -113,6 +113,19 @@ fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fm
 fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                  void* stream);
+
+/* FP32 master-weight input.  [snippets] forward-pass snippet: the master
+ * weights are FP32 and are quantised to FP8 for the GEMM.  The same calls as
+ * fp8_amax and fp8_quantize_tensor for an FP32 tensor: amax is the largest
+ * |x| under NaN > inf > finite on the FP32 magnitude bits (exactly an FP32
+ * value); the cast is sat_rne(fl32(x * scale)).  Shapes, alignment (16-byte
+ * data) and errors as for the BF16 calls; the workspace note under Memory
+ * applies to fp8_amax_f32 and to fp8_quantize_tensor_f32 with amax_out. */
+fp8_status_t fp8_amax_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
+                          float* amax, float* scale, float* scale_inv, void* stream);
+fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
+                                     const float* scale, uint8_t* q, uint8_t* qT,
+                                     float* amax_out, void* stream);
 
 /* One delayed-scaling step.  [guide] delayed scaling keeps a buffer of the
  * maxima of past steps; [colossal] delayed scaling takes the scale from a
@@ -215,6 +228,20 @@ fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, in
                             int64_t N, int64_t K, void* dx_bf16, void* stream);
 fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
                             int64_t N, int64_t K, void* dw_bf16, void* stream);
+
+/* wgrad with an FP32 result, optionally accumulated.  [snippets] forward-
+ * pass snippet: the master weights are FP32, so their gradient is too;
+ * accumulating into it is how a weight gradient sums over micro-batches.
+ *   dw_f32[N][K] = (accumulate ? dw_f32 : 0) + the wgrad sum of
+ *                  fp8_gemm_wgrad (same operands, scaling and shape rules),
+ * computed in FP32 and stored without rounding to BF16; with accumulate the
+ * previous value is added in FP32 (one rounding).
+ *   accumulate  0 or 1 (else FP8_ERR_UNSUPPORTED)
+ *   dw_f32      in/out float [N][K], 16-byte aligned
+ * Errors: as fp8_gemm_wgrad. */
+fp8_status_t fp8_gemm_wgrad_f32(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
+                                int64_t N, int64_t K, float* dw_f32, int32_t accumulate,
+                                void* stream);
 
 /* The cast's rounding step alone: q[i] = cast(x[i]) for FP32 inputs (no
  * scaling).  Every quantise kernel above rounds through the same device

@@ -218,6 +218,41 @@ void oracle_quantize_tensor(const uint16_t* x, int64_t rows, int64_t cols, int f
   if (amax_out) *amax_out = oracle_amax(x, rows * cols);
 }
 
+/* ---------------------------------------------- FP32 master-weight input */
+
+/* The same amax and cast for an FP32 tensor ([snippets] forward-pass
+ * snippet: the master weights are FP32 and are quantised to FP8).  amax is
+ * the largest |x| under the same total order, now on the FP32 magnitude bits
+ * (bits & 0x7FFFFFFF): NaN > inf > every finite value; the result is exactly
+ * an FP32 value.  The cast is the BF16 one without the widening:
+ * q = sat_rne(fl32(x * scale)). */
+float oracle_amax_f32(const float* x, int64_t n) {
+  uint32_t m = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t b;
+    memcpy(&b, &x[i], 4);
+    b &= 0x7FFFFFFFu;
+    if (b > m) m = b;
+  }
+  float a;
+  memcpy(&a, &m, 4);
+  return a;
+}
+
+void oracle_quantize_tensor_f32(const float* x, int64_t rows, int64_t cols, int fmt,
+                                float scale, uint8_t* q, uint8_t* qT, float* amax_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      float p = x[r * cols + c] * scale;
+      uint8_t code = oracle_fp8_encode(p, fmt);
+      if (q) q[r * cols + c] = code;
+      if (qT) qT[c * rows + r] = code;
+    }
+  }
+  if (amax_out) *amax_out = oracle_amax_f32(x, rows * cols);
+}
+
 /* ------------------------------------------------------- delayed scaling */
 
 /* One history step.  [colossal] delayed scaling computes the current scale

@@ -67,6 +67,12 @@ def lib():
         L.oracle_quantize_tensor.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_amax_f32.restype = ctypes.c_float
+        L.oracle_amax_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        L.oracle_quantize_tensor_f32.restype = None
+        L.oracle_quantize_tensor_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_amax_history_update.restype = None
         L.oracle_amax_history_update.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                                  ctypes.c_float, ctypes.c_int,
@@ -168,6 +174,25 @@ def quantize_tensor(x, fmt: int, scale, transposed: bool = False, want_amax: boo
     lib().oracle_quantize_tensor(_p(x), R, C, fmt, float(np.float32(scale)), _p(q),
                                  _p(qT) if qT is not None else None,
                                  _p(am) if want_amax else None)
+    return q, qT, (np.float32(am[0]) if want_amax else None)
+
+
+def amax_f32(x) -> float:
+    """amax of an FP32 array (FP32 master weight)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return float(np.float32(lib().oracle_amax_f32(_p(x), x.size)))
+
+
+def quantize_tensor_f32(x, fmt: int, scale, transposed: bool = False, want_amax: bool = False):
+    """Per-tensor cast of an FP32 array; returns (q, qT or None, amax or None)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, C = x.shape
+    q = np.empty((R, C), np.uint8)
+    qT = np.empty((C, R), np.uint8) if transposed else None
+    am = np.zeros(1, np.float32)
+    lib().oracle_quantize_tensor_f32(_p(x), R, C, fmt, float(np.float32(scale)), _p(q),
+                                     _p(qT) if qT is not None else None,
+                                     _p(am) if want_amax else None)
     return q, qT, (np.float32(am[0]) if want_amax else None)
 
 

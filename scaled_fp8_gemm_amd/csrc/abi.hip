@@ -33,7 +33,7 @@ bool is_block(int32_t sc) { return sc == FP8_SCALE_BLOCK_1x128 || sc == FP8_SCAL
 
 // C[rows_a][rows_b] = A[rows_a][kc] . B[rows_b][kc]^T with the operands' scales.
 fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a,
-                  int64_t rows_b, int64_t kc, void* c, void* stream) {
+                  int64_t rows_b, int64_t kc, void* c, void* stream, int out = 0) {
   if (!a || !b) return FP8_ERR_NULL;
   if (!fmt_ok(a->fmt) || !fmt_ok(b->fmt)) return FP8_ERR_UNSUPPORTED;
   if (a->scaling < FP8_SCALE_TENSOR || a->scaling > FP8_SCALE_MX_1x32 ||
@@ -69,7 +69,8 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   p.B = b->data;
   p.sa = a->scale_inv;
   p.sb = b->scale_inv;
-  p.C = static_cast<uint16_t*>(c);
+  p.C = c;
+  p.out = out;
   p.M = rows_a;
   p.N = rows_b;
   p.K = kc;
@@ -81,36 +82,59 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   return hip(fp8sg::launch_gemm(p, st(stream)));
 }
 
+// amax / per-tensor cast of BF16 (in = 0) or FP32 (in = 1) input.
+fp8_status_t amax_any(const void* x, int64_t rows, int64_t cols, int32_t fmt, float* amax,
+                      float* scale, float* scale_inv, void* stream, int in) {
+  if (!amax) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x, rows * cols)) return FP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(amax, 4) || (scale && !aligned(scale, 4)) ||
+      (scale_inv && !aligned(scale_inv, 4)))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_amax(x, rows * cols, fmt, amax, scale, scale_inv, st(stream), in));
+}
+
+fp8_status_t quantize_tensor_any(const void* x, int64_t rows, int64_t cols, int32_t fmt,
+                                 const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                 void* stream, int in) {
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x, rows * cols) || !have(q, rows * cols) || !have(scale, rows * cols))
+    return FP8_ERR_NULL;
+  if (cols % 16) return FP8_ERR_ALIGN;
+  if (qT && rows % 16) return FP8_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) || !aligned(scale, 4) ||
+      (amax_out && !aligned(amax_out, 4)))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_tensor(x, rows, cols, fmt, scale, q, qT, amax_out,
+                                           st(stream), in));
+}
+
 }  // namespace
 
 extern "C" {
 
 fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt, float* amax,
                       float* scale, float* scale_inv, void* stream) {
-  if (!amax) return FP8_ERR_NULL;
-  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
-  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
-  if (!have(x_bf16, rows * cols)) return FP8_ERR_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(amax, 4) || (scale && !aligned(scale, 4)) ||
-      (scale_inv && !aligned(scale_inv, 4)))
-    return FP8_ERR_ALIGN;
-  return hip(fp8sg::launch_amax(x_bf16, rows * cols, fmt, amax, scale, scale_inv, st(stream)));
+  return amax_any(x_bf16, rows, cols, fmt, amax, scale, scale_inv, stream, 0);
+}
+
+fp8_status_t fp8_amax_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
+                          float* amax, float* scale, float* scale_inv, void* stream) {
+  return amax_any(x_f32, rows, cols, fmt, amax, scale, scale_inv, stream, 1);
 }
 
 fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                  void* stream) {
-  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
-  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
-  if (!have(x_bf16, rows * cols) || !have(q, rows * cols) || !have(scale, rows * cols))
-    return FP8_ERR_NULL;
-  if (cols % 16) return FP8_ERR_ALIGN;
-  if (qT && rows % 16) return FP8_ERR_ALIGN;
-  if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||
-      !aligned(scale, 4) || (amax_out && !aligned(amax_out, 4)))
-    return FP8_ERR_ALIGN;
-  return hip(fp8sg::launch_quantize_tensor(x_bf16, rows, cols, fmt, scale, q, qT, amax_out,
-                                           st(stream)));
+  return quantize_tensor_any(x_bf16, rows, cols, fmt, scale, q, qT, amax_out, stream, 0);
+}
+
+fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
+                                     const float* scale, uint8_t* q, uint8_t* qT,
+                                     float* amax_out, void* stream) {
+  return quantize_tensor_any(x_f32, rows, cols, fmt, scale, q, qT, amax_out, stream, 1);
 }
 
 fp8_status_t fp8_amax_history_update(float* history, int32_t history_len, int64_t step,
@@ -194,6 +218,13 @@ fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, in
 fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
                             int64_t N, int64_t K, void* dw_bf16, void* stream) {
   return gemm(dyT, xT, N, K, M, dw_bf16, stream);
+}
+
+fp8_status_t fp8_gemm_wgrad_f32(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
+                                int64_t N, int64_t K, float* dw_f32, int32_t accumulate,
+                                void* stream) {
+  if (accumulate != 0 && accumulate != 1) return FP8_ERR_UNSUPPORTED;
+  return gemm(dyT, xT, N, K, M, dw_f32, stream, accumulate ? 2 : 1);
 }
 
 fp8_status_t fp8_convert_f32(const float* x, int64_t n, int32_t fmt, uint8_t* q, void* stream) {

@@ -191,11 +191,10 @@ void k_gemm8(Args p) {
     __syncthreads();
   }
 
-  // Epilogue: scale (tensor mode), round to BF16, 8-byte stores.
+  // Epilogue: scale (tensor mode), then BF16 / FP32 / FP32-accumulate stores.
   float s = 1.0f;
   if constexpr (MODE == kTensor)
     s = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sb)[0];
-  const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int64_t m = m_base + f * 16 + lr;
@@ -205,17 +204,7 @@ void k_gemm8(Args p) {
       const int64_t n = n_base + j * 16 + 4 * g;
       if (n >= p.N) continue;
       const v4f a = acc[f][j];
-      uint16_t* dst = p.C + m * p.N + n;
-      if (vec_ok) {
-        uint2 o;
-        o.x = pack_bf16x2(a[0] * s, a[1] * s);
-        o.y = pack_bf16x2(a[2] * s, a[3] * s);
-        *reinterpret_cast<uint2*>(dst) = o;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < p.N) dst[r] = (uint16_t)(pack_bf16x2(a[r] * s, 0.f) & 0xffffu);
-      }
+      store4(p, m, n, a[0] * s, a[1] * s, a[2] * s, a[3] * s);
     }
   }
 }
@@ -223,7 +212,7 @@ void k_gemm8(Args p) {
 template <int MODE, int FA, int FB, int BRA, int BRB>
 hipError_t run(const GemmProblem& q, hipStream_t s) {
   Args a;
-  a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C;
+  a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C; a.out = q.out;
   a.M = q.M; a.N = q.N; a.K = q.K;
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);

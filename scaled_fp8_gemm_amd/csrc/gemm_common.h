@@ -30,10 +30,49 @@ struct Args {
   const uint8_t* B;
   const void* sa;
   const void* sb;
-  uint16_t* C;
+  void* C;
   int64_t M, N, K;
   int tiles_m, tiles_n;
+  int out;      // 0: BF16 C; 1: FP32 C; 2: FP32 C += result
 };
+
+// Four consecutive outputs of row m, columns n .. n+3 (columns past N are
+// dropped): rounded to BF16 (nearest even), stored as FP32, or added in FP32
+// to what C holds.  16-byte / 8-byte vector stores when N % 4 == 0.
+__device__ __forceinline__ void store4(const Args& p, int64_t m, int64_t n, float a0, float a1,
+                                       float a2, float a3) {
+  const int64_t off = m * p.N + n;
+  const bool vec = (p.N & 3) == 0;
+  const float v[4] = {a0, a1, a2, a3};
+  if (p.out == 0) {
+    uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
+    if (vec) {
+      uint2 o;
+      o.x = pack_bf16x2(a0, a1);
+      o.y = pack_bf16x2(a2, a3);
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < p.N) dst[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xffffu);
+    }
+  } else {
+    float* dst = static_cast<float*>(p.C) + off;
+    const bool acc = p.out == 2;
+    if (vec) {
+      float4 o = make_float4(a0, a1, a2, a3);
+      if (acc) {
+        const float4 c = *reinterpret_cast<const float4*>(dst);
+        o = make_float4(c.x + a0, c.y + a1, c.z + a2, c.w + a3);
+      }
+      *reinterpret_cast<float4*>(dst) = o;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < p.N) dst[r] = acc ? dst[r] + v[r] : v[r];
+    }
+  }
+}
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

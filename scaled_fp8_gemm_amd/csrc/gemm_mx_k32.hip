@@ -109,7 +109,6 @@ void k_gemm_mx_k32(Args p) {
     __syncthreads();
   }
 
-  const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int64_t m = m_base + f * 16 + lr;
@@ -119,17 +118,7 @@ void k_gemm_mx_k32(Args p) {
       const int64_t n = n_base + j * 16 + 4 * g;
       if (n >= p.N) continue;
       const v4f a = acc[f][j];
-      uint16_t* dst = p.C + m * p.N + n;
-      if (vec_ok) {
-        uint2 o;
-        o.x = pack_bf16x2(a[0], a[1]);
-        o.y = pack_bf16x2(a[2], a[3]);
-        *reinterpret_cast<uint2*>(dst) = o;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < p.N) dst[r] = (uint16_t)(pack_bf16x2(a[r], 0.f) & 0xffffu);
-      }
+      store4(p, m, n, a[0], a[1], a[2], a[3]);
     }
   }
 }
@@ -137,7 +126,7 @@ void k_gemm_mx_k32(Args p) {
 template <int FA, int FB>
 hipError_t run(const GemmProblem& q, hipStream_t s) {
   Args a;
-  a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C;
+  a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C; a.out = q.out;
   a.M = q.M; a.N = q.N; a.K = q.K;
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);

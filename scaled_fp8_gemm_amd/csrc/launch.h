@@ -9,11 +9,12 @@ namespace fp8sg {
 
 int device_cu_count();
 
+// in: 0 = BF16 input, 1 = FP32 input
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
-                       float* scale_inv, hipStream_t s);
+                       float* scale_inv, hipStream_t s, int in);
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                  hipStream_t s);
+                                  hipStream_t s, int in);
 hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
                                  float* scale, float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,
@@ -33,11 +34,12 @@ struct GemmProblem {
   const uint8_t* B;
   const void* sa;
   const void* sb;
-  uint16_t* C;
+  void* C;
   int64_t M, N, K;
   int fa, fb;
   int mode;
   int bra, brb;
+  int out;      // 0: BF16 C; 1: FP32 C; 2: FP32 C += result
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_mx_k32(const GemmProblem& p, hipStream_t s);

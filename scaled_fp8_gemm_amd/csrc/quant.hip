@@ -33,10 +33,27 @@ constexpr int kMaxPartials = 2048;
 // workgroup c mod gridDim.x; the last chunk is predicated.
 constexpr int kChunkLoads = 4;
 
-// amax over n BF16 values: nvec 16-byte vectors plus a tail of < 8 elements.
-// part[blockIdx.x] = the workgroup's largest BF16 magnitude (bits & 0x7fff).
+// Input element types: BF16 (the activations, gradients and BF16 master
+// weights) or FP32 (an FP32 master weight).  Maxima are kept as FP32
+// magnitude bits (a BF16 magnitude shifted left by 16), which order like the
+// values: NaN > inf > finite.
+enum : int { kInBF16 = 0, kInF32 = 1 };
+
+// Largest magnitude (FP32 bits) in one 16-byte vector of either type.
+template <int IN>
+__device__ __forceinline__ uint32_t vec_absmax(uint4 v) {
+  if constexpr (IN == kInBF16) {
+    return absmax8(v) << 16;
+  } else {
+    return max(max(v.x & 0x7fffffffu, v.y & 0x7fffffffu), max(v.z & 0x7fffffffu, v.w & 0x7fffffffu));
+  }
+}
+
+// amax over n values: nvec 16-byte vectors plus a tail of fewer elements than
+// a vector holds.  part[blockIdx.x] = the workgroup's largest magnitude.
+template <int IN>
 __global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ x, int64_t nvec,
-                                                   const uint16_t* __restrict__ tail, int ntail,
+                                                   const void* __restrict__ tail, int ntail,
                                                    uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
   constexpr int U = kChunkLoads;
@@ -49,19 +66,24 @@ __global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ x, 
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[i + u * kThreads]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
+      for (int u = 0; u < U; ++u) m = max(m, vec_absmax<IN>(v[u]));
     } else {
       for (int u = 0; u < U; ++u)
-        if (i + u * kThreads < nvec) m = max(m, absmax8(ld_stream(&x[i + u * kThreads])));
+        if (i + u * kThreads < nvec) m = max(m, vec_absmax<IN>(ld_stream(&x[i + u * kThreads])));
     }
   }
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7fffu));
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
+    if constexpr (IN == kInBF16)
+      m = max(m, (uint32_t)(static_cast<const uint16_t*>(tail)[threadIdx.x] & 0x7fffu) << 16);
+    else
+      m = max(m, static_cast<const uint32_t*>(tail)[threadIdx.x] & 0x7fffffffu);
+  }
   m = block_max_u32<kThreads>(m, red);
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-// Reduce n partial maxima to the tensor's amax (a BF16 magnitude widened to
-// FP32 bits) and, where asked, the scale pair derived from it.
+// Reduce n partial maxima (FP32 magnitude bits) to the tensor's amax and,
+// where asked, the scale pair derived from it.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __restrict__ part,
                                                             int n, float* __restrict__ amax,
@@ -72,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
   for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, part[i]);
   m = block_max_u32<kThreads>(m, red);
   if (threadIdx.x == 0) {
-    const float a = __uint_as_float(m << 16);
+    const float a = __uint_as_float(m);
     *amax = a;
     if (scale || scale_inv) {
       const float s = scale_from_amax<FMT>(a);
@@ -82,46 +104,73 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
   }
 }
 
-// Per-tensor cast without a transposed copy: a thread casts 16 elements (two
-// 16-byte loads, one 16-byte store) per group; n16 = number of 16-element
-// groups; chunks of kThreads * 2 groups (16 KB of input) per workgroup step.
-template <int FMT>
-__device__ __forceinline__ uint4 cast16(uint4 a, uint4 b, float s) {
-  uint2 qa = cast8<FMT>(a, s), qb = cast8<FMT>(b, s);
-  return make_uint4(qa.x, qa.y, qb.x, qb.y);
-}
+// 16 consecutive elements (16-byte aligned) times s -> 16 FP8 bytes; m takes
+// their largest magnitude.  BF16: two 16-byte loads; FP32: four.
+template <int FMT, int IN>
+struct Row16 {
+  static constexpr int V = IN == kInBF16 ? 2 : 4;   // 16-byte vectors per 16 elements
+  uint4 v[V];
+  __device__ __forceinline__ void load(const void* p) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) v[k] = ld_stream(static_cast<const uint4*>(p) + k);
+  }
+  __device__ __forceinline__ uint32_t absmax() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < V; ++k) m = max(m, vec_absmax<IN>(v[k]));
+    return m;
+  }
+  // the four output words (bytes of elements 4k .. 4k+3 in word k)
+  __device__ __forceinline__ void cast(float s, uint32_t (&w)[4]) const {
+    if constexpr (IN == kInBF16) {
+      const uint2 lo = cast8<FMT>(v[0], s), hi = cast8<FMT>(v[1], s);
+      w[0] = lo.x; w[1] = lo.y; w[2] = hi.x; w[3] = hi.y;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = cvt4<FMT>(__uint_as_float(v[k].x) * s, __uint_as_float(v[k].y) * s,
+                         __uint_as_float(v[k].z) * s, __uint_as_float(v[k].w) * s);
+    }
+  }
+};
 
-template <int FMT, bool AMAX>
-__global__ __launch_bounds__(kThreads) void k_cast(const uint4* __restrict__ x, int64_t n16,
+// Per-tensor cast without a transposed copy: a thread casts 16 elements (one
+// 16-byte store) per group; n16 = number of 16-element groups; chunks of
+// kThreads * 2 groups per workgroup step.
+template <int FMT, bool AMAX, int IN>
+__global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x, int64_t n16,
                                                    const float* __restrict__ scale_p,
                                                    uint4* __restrict__ q,
                                                    uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
-  constexpr int U = kChunkLoads / 2;
+  constexpr int U = 2;
+  constexpr int64_t GB = 16 * (IN == kInBF16 ? 2 : 4);   // input bytes per group
   const float s = *scale_p;
   uint32_t m = 0;
   const int64_t nchunks = (n16 + kThreads * U - 1) / (kThreads * U);
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     const int64_t i = c * (kThreads * U) + threadIdx.x;
     if (i + (U - 1) * kThreads < n16) {
-      uint4 a[U], b[U];
+      Row16<FMT, IN> r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u].load(x + (i + u * kThreads) * GB);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        a[u] = ld_stream(&x[2 * (i + u * kThreads)]);
-        b[u] = ld_stream(&x[2 * (i + u * kThreads) + 1]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (AMAX) m = max(m, max(absmax8(a[u]), absmax8(b[u])));
-        q[i + u * kThreads] = cast16<FMT>(a[u], b[u], s);
+        if (AMAX) m = max(m, r[u].absmax());
+        uint32_t w[4];
+        r[u].cast(s, w);
+        q[i + u * kThreads] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     } else {
       for (int u = 0; u < U; ++u) {
         const int64_t j = i + u * kThreads;
         if (j < n16) {
-          uint4 a0 = ld_stream(&x[2 * j]), b0 = ld_stream(&x[2 * j + 1]);
-          if (AMAX) m = max(m, max(absmax8(a0), absmax8(b0)));
-          q[j] = cast16<FMT>(a0, b0, s);
+          Row16<FMT, IN> r;
+          r.load(x + j * GB);
+          if (AMAX) m = max(m, r.absmax());
+          uint32_t w[4];
+          r.cast(s, w);
+          q[j] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
     }
@@ -164,13 +213,14 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
 // 16-row / 16-column groups).
 __device__ __forceinline__ int qt_word(int col, int a) { return col * 32 + (a ^ (((col >> 4) & 7) << 2)); }
 
-template <int FMT, bool AMAX>
-__global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict__ x, int64_t rows,
+template <int FMT, bool AMAX, int IN>
+__global__ __launch_bounds__(kThreads) void k_cast_t(const uint8_t* __restrict__ x, int64_t rows,
                                                      int64_t cols, int64_t ntx, int64_t ntiles,
                                                      const float* __restrict__ scale_p,
                                                      uint8_t* __restrict__ q,
                                                      uint8_t* __restrict__ qT,
                                                      uint32_t* __restrict__ part) {
+  constexpr int64_t EB = IN == kInBF16 ? 2 : 4;   // bytes per input element
   __shared__ uint32_t red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
   const float s = *scale_p;
@@ -184,20 +234,15 @@ __global__ __launch_bounds__(kThreads) void k_cast_t(const uint16_t* __restrict_
     uint32_t* T = tile[buf];
     uint32_t b[4][4];   // [row i][word k] = columns 16c + 4k .. +3 of row 4a + i
     if (4 * a < rv && 16 * c < cv) {
-      uint4 v[4][2];
+      Row16<FMT, IN> v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i].load(x + ((r0 + 4 * a + i) * cols + c0 + 16 * c) * EB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t* src = x + (r0 + 4 * a + i) * cols + c0 + 16 * c;
-        v[i][0] = ld_stream(src);
-        v[i][1] = ld_stream(src + 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (AMAX) m = max(m, max(absmax8(v[i][0]), absmax8(v[i][1])));
-        const uint2 lo = cast8<FMT>(v[i][0], s), hi = cast8<FMT>(v[i][1], s);
-        b[i][0] = lo.x; b[i][1] = lo.y; b[i][2] = hi.x; b[i][3] = hi.y;
+        if (AMAX) m = max(m, v[i].absmax());
+        v[i].cast(s, b[i]);
         *reinterpret_cast<uint4*>(q + (r0 + 4 * a + i) * cols + c0 + 16 * c) =
-            make_uint4(lo.x, lo.y, hi.x, hi.y);
+            make_uint4(b[i][0], b[i][1], b[i][2], b[i][3]);
       }
     } else {
 #pragma unroll
@@ -643,61 +688,74 @@ int device_cu_count() {
   } while (0)
 
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
-                       float* scale_inv, hipStream_t s) {
+                       float* scale_inv, hipStream_t s, int in) {
   uint32_t* part = nullptr;
   hipError_t err = stream_partials(s, &part);
   if (err != hipSuccess) return err;
-  const int64_t nvec = n / 8;
-  const int ntail = (int)(n - nvec * 8);
-  const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
+  const int per = in == kInBF16 ? 8 : 4;   // elements per 16-byte vector
+  const int64_t nvec = n / per;
+  const int ntail = (int)(n - nvec * per);
+  const void* tail = static_cast<const uint8_t*>(x) + nvec * 16;
   int g = 1;
   if (n > 0) {
     g = grid_for(nvec > 0 ? nvec : 1, kThreads * kChunkLoads);
-    hipLaunchKernelGGL(k_amax, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(x),
-                       nvec, tail, ntail, part);
+    if (in == kInBF16)
+      hipLaunchKernelGGL(k_amax<kInBF16>, dim3(g), dim3(kThreads), 0, s,
+                         static_cast<const uint4*>(x), nvec, tail, ntail, part);
+    else
+      hipLaunchKernelGGL(k_amax<kInF32>, dim3(g), dim3(kThreads), 0, s,
+                         static_cast<const uint4*>(x), nvec, tail, ntail, part);
   }
   FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,
                                              part, n > 0 ? g : 0, amax, scale, scale_inv));
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
-                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                  hipStream_t s) {
-  uint32_t* part = nullptr;
-  if (amax_out) {
-    hipError_t err = stream_partials(s, &part);
-    if (err != hipSuccess) return err;
-  }
+template <int IN>
+static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, const float* scale,
+                         uint8_t* q, uint8_t* qT, uint32_t* part, int& g, hipStream_t s) {
   const int64_t n = rows * cols;
-  int g = 0;
-  if (n > 0 && qT) {
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  if (qT) {
     const int64_t ntx = (cols + 127) / 128;
     const int64_t ntiles = ntx * ((rows + 127) / 128);
     g = grid_for(ntiles, 1);
     FP8SG_FMT_DISPATCH(fmt, {
       if (part)
-        hipLaunchKernelGGL((k_cast_t<F, true>), dim3(g), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(x), rows, cols, ntx, ntiles, scale, q, qT,
-                           part);
+        hipLaunchKernelGGL((k_cast_t<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, rows, cols,
+                           ntx, ntiles, scale, q, qT, part);
       else
-        hipLaunchKernelGGL((k_cast_t<F, false>), dim3(g), dim3(kThreads), 0, s,
-                           static_cast<const uint16_t*>(x), rows, cols, ntx, ntiles, scale, q, qT,
-                           part);
+        hipLaunchKernelGGL((k_cast_t<F, false, IN>), dim3(g), dim3(kThreads), 0, s, xb, rows,
+                           cols, ntx, ntiles, scale, q, qT, part);
     });
-  } else if (n > 0) {
+  } else {
     const int64_t n16 = n / 16;
-    g = grid_for(n16, kThreads * (kChunkLoads / 2));
+    g = grid_for(n16, kThreads * 2);
     FP8SG_FMT_DISPATCH(fmt, {
       if (part)
-        hipLaunchKernelGGL((k_cast<F, true>), dim3(g), dim3(kThreads), 0, s,
-                           static_cast<const uint4*>(x), n16, scale,
+        hipLaunchKernelGGL((k_cast<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, scale,
                            reinterpret_cast<uint4*>(q), part);
       else
-        hipLaunchKernelGGL((k_cast<F, false>), dim3(g), dim3(kThreads), 0, s,
-                           static_cast<const uint4*>(x), n16, scale,
+        hipLaunchKernelGGL((k_cast<F, false, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, scale,
                            reinterpret_cast<uint4*>(q), part);
     });
+  }
+}
+
+hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
+                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
+                                  hipStream_t s, int in) {
+  uint32_t* part = nullptr;
+  if (amax_out) {
+    hipError_t err = stream_partials(s, &part);
+    if (err != hipSuccess) return err;
+  }
+  int g = 0;
+  if (rows * cols > 0) {
+    if (in == kInBF16)
+      cast_kernels<kInBF16>(x, rows, cols, fmt, scale, q, qT, part, g, s);
+    else
+      cast_kernels<kInF32>(x, rows, cols, fmt, scale, q, qT, part, g, s);
   }
   if (part)
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,

@@ -38,9 +38,11 @@ class Operand(ctypes.Structure):
 
 
 _lib = None
-_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_amax_history_update", "fp8_quantize_block",
+_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_amax_f32", "fp8_quantize_tensor_f32",
+            "fp8_amax_history_update", "fp8_quantize_block",
             "fp8_quantize_mx", "fp8_quantize_block_t", "fp8_quantize_mx_t", "fp8_gemm_fprop",
-            "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_convert_f32", "fp8_status_string"]
+            "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_gemm_wgrad_f32", "fp8_convert_f32",
+            "fp8_status_string"]
 
 
 def lib():
@@ -55,6 +57,8 @@ def lib():
         sig = {
             "fp8_amax": [vp, i64, i64, i32, vp, vp, vp, vp],
             "fp8_quantize_tensor": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
+            "fp8_amax_f32": [vp, i64, i64, i32, vp, vp, vp, vp],
+            "fp8_quantize_tensor_f32": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_amax_history_update": [vp, i32, i64, vp, i32, vp, vp, vp],
             "fp8_quantize_block": [vp, i64, i64, i32, i32, i32, vp, vp, vp],
             "fp8_quantize_mx": [vp, i64, i64, i32, vp, vp, vp],
@@ -63,6 +67,7 @@ def lib():
             "fp8_gemm_fprop": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_dgrad": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_wgrad": [vp, vp, i64, i64, i64, vp, vp],
+            "fp8_gemm_wgrad_f32": [vp, vp, i64, i64, i64, vp, i32, vp],
             "fp8_convert_f32": [vp, i64, i32, vp, vp],
         }
         for name, args in sig.items():
@@ -106,6 +111,19 @@ def fp8_quantize_tensor(x, fmt, scale, q, qT=None, amax_out=None, stream=None):
     _check("fp8_quantize_tensor",
            lib().fp8_quantize_tensor(_ptr(x), rows, cols, fmt, _ptr(scale), _ptr(q), _ptr(qT),
                                      _ptr(amax_out), _stream(stream)))
+
+
+def fp8_amax_f32(x, fmt, amax, scale=None, scale_inv=None, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_amax_f32", lib().fp8_amax_f32(_ptr(x), rows, cols, fmt, _ptr(amax), _ptr(scale),
+                                              _ptr(scale_inv), _stream(stream)))
+
+
+def fp8_quantize_tensor_f32(x, fmt, scale, q, qT=None, amax_out=None, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_quantize_tensor_f32",
+           lib().fp8_quantize_tensor_f32(_ptr(x), rows, cols, fmt, _ptr(scale), _ptr(q), _ptr(qT),
+                                         _ptr(amax_out), _stream(stream)))
 
 
 def fp8_amax_history_update(history, step, amax, fmt, scale, scale_inv, stream=None):
@@ -159,6 +177,12 @@ def fp8_gemm_dgrad(dy: Operand, wT: Operand, M, N, K, dx, stream=None):
 def fp8_gemm_wgrad(dyT: Operand, xT: Operand, M, N, K, dw, stream=None):
     _check("fp8_gemm_wgrad", lib().fp8_gemm_wgrad(ctypes.byref(dyT), ctypes.byref(xT), M, N, K,
                                                   _ptr(dw), _stream(stream)))
+
+
+def fp8_gemm_wgrad_f32(dyT: Operand, xT: Operand, M, N, K, dw, accumulate=False, stream=None):
+    _check("fp8_gemm_wgrad_f32",
+           lib().fp8_gemm_wgrad_f32(ctypes.byref(dyT), ctypes.byref(xT), M, N, K, _ptr(dw),
+                                    1 if accumulate else 0, _stream(stream)))
 
 
 def fp8_convert_f32(x, fmt, q, stream=None):

@@ -190,3 +190,31 @@ def compare(orc, g_bits, r_val, absdot, T, S, label="", realistic=False):
         assert p99 <= 2, f"{label}: p99 ulp {p99}"
     return {"max_rel": max_rel, "p99_ulp": p99, "max_ulp": int(ulps.max()),
             "median_ulp": float(np.median(ulps)), "n": int(g.size)}
+
+
+def check_gemm_f32(orc, g, A, B, fa, fb, mode, sa, sb, bra=1, brb=1, old=None, label=""):
+    """Full-matrix parity of an FP32 GEMM output g (numpy float32) against
+    the oracle's FP64 value r, plus `old` when the output accumulates:
+    |g - (old + r)| <= T + (3S + 4) 2^-24 sum|terms| + 2^-24 (|g| + |old|)
+    (MFMA truncation, FP32 accumulation steps, the scale product and the final
+    FP32 add); and max-relative <= 1e-2."""
+    mode_o = {0: orc.SCALE_TENSOR, 1: orc.SCALE_BLOCK, 2: orc.SCALE_MX}[mode]
+    Cx, Cabs, _ = orc.gemm_full(A, B, fa, fb, mode_o, sa, sb, bra, brb)
+    R, K = np.asarray(A).shape
+    C = np.asarray(B).shape[0]
+    S = (K + MFMA_K - 1) // MFMA_K
+    Ad, Bd = _decode(orc, A, B, fa, fb, mode, sa, sb)
+    Ts = truncation_per_step(Ad, Bd) if S > 0 else np.zeros((R, C, 0))
+    T = (Ts * _step_scales(mode, sa, sb, R, C, S, bra, brb)).sum(axis=-1)
+    g = np.asarray(g, np.float64)
+    o = np.zeros_like(g) if old is None else np.asarray(old, np.float64)
+    want = o + Cx
+    err = np.abs(g - want)
+    bound = T + (3 * S + 4) * 2.0 ** -24 * Cabs + 2.0 ** -24 * (np.abs(g) + np.abs(o)) + 2.0 ** -120
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{label}: {len(bad)} elements outside the bound; first {tuple(bad[0])}: "
+                           f"gpu {g[tuple(bad[0])]} want {want[tuple(bad[0])]}")
+    mr = np.max(np.abs(want))
+    rel = float(err.max() / mr) if mr > 0 else 0.0
+    assert rel <= 1e-2, f"{label}: max-relative {rel}"
+    return rel

@@ -84,6 +84,18 @@ def test_block_and_mx_errors(L):
     assert m(PU, 4, 64, 0, P, P, None) == ALIGN
 
 
+def test_f32_input_errors(L):
+    a = L.fp8_amax_f32
+    assert a(P, 4, 16, 0, None, None, None, None) == NULL
+    assert a(P, -1, 16, 0, P, None, None, None) == SHAPE
+    assert a(PU, 4, 16, 0, P, None, None, None) == ALIGN
+    assert a(P, 4, 16, 3, P, None, None, None) == UNSUP
+    q = L.fp8_quantize_tensor_f32
+    assert q(P, 4, 24, 0, P, P, None, None, None) == ALIGN               # cols % 16
+    assert q(P, 8, 16, 0, P, P, P, None, None) == ALIGN                  # qT needs rows % 16
+    assert q(None, 4, 16, 0, P, P, None, None, None) == NULL
+
+
 def test_transposed_block_and_mx_errors(L):
     bt = L.fp8_quantize_block_t
     assert bt(P, 128, 256, 0, 2, P, P, P, P, None) == UNSUP           # block_rows
@@ -127,6 +139,10 @@ def test_gemm_errors(L):
     assert g(r(t), r(t), 16, 16, (1 << 23) + 16, P, None) == SHAPE        # K > 2^23
     assert g(r(t), r(t), 16, 16, 16, PU, None) == ALIGN
     assert g(r(_op(0, 0, data=PU)), r(t), 16, 16, 16, P, None) == ALIGN
+    wf = L.fp8_gemm_wgrad_f32
+    assert wf(r(t), r(t), 16, 16, 16, P, 2, None) == UNSUP             # accumulate flag
+    assert wf(r(t), r(t), 24, 16, 16, P, 0, None) == ALIGN             # M % 16
+    assert wf(r(t), r(t), 16, 16, 16, None, 1, None) == NULL
     # dgrad contracts over N, wgrad over M
     assert L.fp8_gemm_dgrad(r(t), r(t), 16, 24, 16, P, None) == ALIGN
     assert L.fp8_gemm_wgrad(r(t), r(t), 24, 16, 16, P, None) == ALIGN

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import DEV, bits16, bytes8, check_gemm, dev_bf16, dev_f32, dev_u8, f32
+from tests.gpu_helpers import (DEV, bits16, bytes8, check_gemm, check_gemm_f32, dev_bf16,
+                                dev_f32, dev_u8, f32)
 from tests.test_gpu_quant import rand_bits
 
 pytestmark = pytest.mark.gpu
@@ -214,3 +215,50 @@ def test_layer_three_gemms_mx(F, orc, M, K, N):
                realistic=True)
     check_gemm(orc, bits16(dw), h(gqT), h(xqT), E4M3, E4M3, 2, h(geT), h(xeT), label="mx wgrad",
                realistic=True)
+
+
+# wgrad's output dw[N][K]: K = 90 exercises the scalar (N % 4 != 0) store path
+@pytest.mark.parametrize("scaling", ["tensor", "block", "mx", "mx_k32"])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (384, 72, 90)])
+def test_wgrad_f32_store_and_accumulate(F, orc, scaling, M, N, K):
+    """FP32 wgrad: stored, then accumulated onto a previous FP32 gradient."""
+    if scaling == "block" and (M % 128 or K % 128 or N % 128):
+        pytest.skip("blockwise needs 128-multiples")
+    if scaling == "mx_k32":
+        M = 352                                   # MX contraction % 128 != 0
+    fa, fb = (E5M2, E4M3) if scaling == "tensor" else (E4M3, E4M3)
+    A = rand_codes((N, M), fa, 61)                # dy^T
+    B = rand_codes((K, M), fb, 62)                # x^T
+    rng = np.random.Generator(np.random.PCG64(63))
+    if scaling == "tensor":
+        sca = scb = TENSOR
+        sa, sb = np.float32([0.37]), np.float32([1.75])
+        mode, bra, brb = 0, 1, 1
+    elif scaling == "block":
+        sca = scb = B1
+        sa = (rng.random((N, M // 128)) + 0.5).astype(np.float32)
+        sb = (rng.random((K, M // 128)) + 0.5).astype(np.float32)
+        mode, bra, brb = 1, 1, 1
+    else:
+        sca = scb = MX
+        sa = rng.integers(120, 134, size=(N, M // 32)).astype(np.uint8)
+        sb = rng.integers(120, 134, size=(K, M // 32)).astype(np.uint8)
+        mode, bra, brb = 2, 1, 1
+    Ad, Bd = dev_u8(A), dev_u8(B)
+    sad = dev_u8(sa) if sca == MX else dev_f32(sa)
+    sbd = dev_u8(sb) if scb == MX else dev_f32(sb)
+    oa, ob = F.operand(Ad, fa, sca, sad), F.operand(Bd, fb, scb, sbd)
+    dw = torch.full((N, K), float("nan"), dtype=torch.float32, device=DEV)
+    F.fp8_gemm_wgrad_f32(oa, ob, M, N, K, dw, accumulate=False)
+    torch.cuda.synchronize()
+    g1 = dw.cpu().numpy().copy()
+    check_gemm_f32(orc, g1, A, B, fa, fb, mode, sa, sb, bra, brb, label=f"{scaling} store")
+    old = (rng.standard_normal((N, K)) * np.abs(g1).max()).astype(np.float32)
+    dw.copy_(torch.from_numpy(old))
+    F.fp8_gemm_wgrad_f32(oa, ob, M, N, K, dw, accumulate=True)
+    torch.cuda.synchronize()
+    g2 = dw.cpu().numpy()
+    check_gemm_f32(orc, g2, A, B, fa, fb, mode, sa, sb, bra, brb, old=old,
+                   label=f"{scaling} accumulate")
+    # store then accumulate agree with one FP32 add of the stored result
+    assert np.array_equal(g2, (old + g1).astype(np.float32))

@@ -153,6 +153,56 @@ def test_quantize_mx(F, orc, shape, fmt):
     assert np.array_equal(bytes8(q), wq)
 
 
+def rand_f32(shape, seed, scale=1.0):
+    """FP32 values with a wide magnitude range and a few specials."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = (rng.standard_normal(shape) * np.exp(rng.standard_normal(shape) * 2) * scale)
+    f = f.astype(np.float32)
+    if f.size >= 16:
+        flat = f.reshape(-1)
+        flat[1] = -0.0
+        flat[2] = np.float32(1e-45)                           # FP32 subnormal
+        flat[3] = np.float32(3.4e38)
+    return f
+
+
+# FP32 master weights: 4 elements per 16-byte vector, so the tails differ from BF16
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (37, 41), (1000, 1003), (2056, 8208)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_amax_f32(F, orc, shape, fmt):
+    x = rand_f32(shape, 81 + shape[0])
+    am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+    F.fp8_amax_f32(torch.from_numpy(x).to(DEV), fmt, am, s, si)
+    wa = orc.amax_f32(x)
+    ws, wsi = orc.scale_from_amax(wa, fmt)
+    assert f32(am)[0].view(np.uint32) == np.float32(wa).view(np.uint32)
+    assert f32(s)[0] == ws and f32(si)[0] == wsi
+    x[0, 0] = np.float32(np.nan)
+    F.fp8_amax_f32(torch.from_numpy(x).to(DEV), fmt, am, s, si)
+    assert np.isnan(f32(am)[0]) and f32(s)[0] == 1.0
+
+
+@pytest.mark.parametrize("shape,transposed", [((1, 16), False), ((37, 48), False),
+                                              ((48, 400), True), ((272, 384), True),
+                                              ((4112, 8208), False), ((4112, 8208), True)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_tensor_f32(F, orc, shape, transposed, fmt):
+    x = rand_f32(shape, 91 + shape[1], 10.0)
+    R, C = shape
+    xd = torch.from_numpy(x).to(DEV)
+    s = torch.tensor([0.7310586], dtype=torch.float32, device=DEV)
+    q = empty_dev(shape, torch.uint8)
+    qT = empty_dev((C, R), torch.uint8) if transposed else None
+    am = empty_dev(1, torch.float32)
+    F.fp8_quantize_tensor_f32(xd, fmt, s, q, qT, am)
+    wq, wqT, wam = orc.quantize_tensor_f32(x, fmt, f32(s)[0], transposed=transposed,
+                                           want_amax=True)
+    assert np.array_equal(bytes8(q), wq)
+    if transposed:
+        assert np.array_equal(bytes8(qT), wqT)
+    assert f32(am)[0].view(np.uint32) == np.float32(wam).view(np.uint32)
+
+
 def _specials_in_columns(x):
     """An all-zero column tile, a NaN, a -inf and a largest-BF16 entry in the
     first column tile, so column scales meet every special case."""

@@ -11,7 +11,11 @@ What fixes each result:
 * blockwise (guide, section "blockwise scaling"): uniform tiles reduce to
   per-tensor, an outlier tile leaves the others untouched, brute force per tile;
 * MX (guide, section "MXFP8 scaling"): the E8M0 exponent against an exact
-  rational search over every positive finite BF16 amax.
+  rational search over every positive finite BF16 amax;
+* FP32 master-weight input (fp8+bf8 search-result snippet, forward pass):
+  reduces to the BF16 functions on BF16-exact values, amax equals numpy's
+  max |x| on finite data, the cast equals numpy's FP32 product fed to the
+  encoder that the codec tests pin on all 2^32 inputs.
 """
 import math
 from fractions import Fraction
@@ -219,3 +223,45 @@ def test_mx_cast_blocks(orc):
             assert np.all(np.abs(d - blk) <= np.abs(blk) * 2 ** -4 + scale * 2.0 ** -10)
             if np.any(blk != 0):
                 assert np.max(np.abs(t[q[r, b * 32:(b + 1) * 32]])) >= 224.0 or e[r, b] == 0
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_f32_input_reduces_to_bf16_on_bf16_values(orc, fmt):
+    rng = np.random.Generator(np.random.PCG64(71))
+    f = (rng.standard_normal((48, 80)) * 3).astype(np.float32)
+    f.view(np.uint32)[...] &= 0xFFFF0000                    # BF16-exact values
+    f[3, 7] = np.float32(-np.inf)
+    b = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert orc.amax_f32(f) == orc.amax(b) == np.inf
+    f[3, 7] = 1.0
+    b[3, 7] = 0x3F80
+    a32, a16 = orc.amax_f32(f), orc.amax(b)
+    assert a32 == a16
+    s, _ = orc.scale_from_amax(a16, fmt)
+    q32, qT32, am32 = orc.quantize_tensor_f32(f, fmt, s, transposed=True, want_amax=True)
+    q16, qT16, am16 = orc.quantize_tensor(b, fmt, s, transposed=True, want_amax=True)
+    assert np.array_equal(q32, q16) and np.array_equal(qT32, qT16) and am32 == am16
+
+
+def test_f32_amax_against_numpy(orc):
+    rng = np.random.Generator(np.random.PCG64(72))
+    f = (rng.standard_normal((300, 129)) * np.exp(rng.standard_normal((300, 129)) * 8)).astype(np.float32)
+    assert orc.amax_f32(f) == np.max(np.abs(f))
+    f[5, 5] = np.float32(np.nan)
+    assert np.isnan(orc.amax_f32(f))
+    assert orc.amax_f32(np.zeros((2, 16), np.float32)) == 0.0
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_f32_cast_is_fp32_product_then_encode(orc, fmt):
+    """Values that are not BF16-exact, scales that are not powers of two: the
+    code must come from the FP32 product (one rounding), not a wider one."""
+    rng = np.random.Generator(np.random.PCG64(73))
+    f = (rng.standard_normal((64, 96)) * 50).astype(np.float32)
+    s = np.float32(3.1415927)
+    q, qT, _ = orc.quantize_tensor_f32(f, fmt, s, transposed=True)
+    want = orc.encode(f * s, fmt)                             # numpy FP32 multiply
+    assert np.array_equal(q, want) and np.array_equal(qT, want.T)
+    # products that round differently in FP32 and FP64 exist in this sample
+    p64 = f.astype(np.float64) * np.float64(s)
+    assert np.any(p64 != (f * s).astype(np.float64))
