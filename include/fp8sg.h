@@ -21,8 +21,9 @@
  * Conventions for every call
  *   Memory      Every pointer argument except `stream` is device memory owned by
  *               the caller.  Tensors are dense and row-major.  The calls that
- *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out)
- *               reduce through an 8 KB buffer of partial maxima that the
+ *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out,
+ *               fp8_gemm_fprop_fused with y_amax) reduce through a 256 KB
+ *               buffer of partial maxima that the
  *               library allocates (hipMalloc) on the first such call on each
  *               (device, stream) pair and keeps until the process ends; calls
  *               on one stream run in order and share it, calls on different
@@ -228,6 +229,27 @@ fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, in
                             int64_t N, int64_t K, void* dx_bf16, void* stream);
 fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
                             int64_t N, int64_t K, void* dw_bf16, void* stream);
+
+/* fprop with the next layer's quantisation fused into the epilogue.
+ * [colossal] scaling paragraph: delayed scaling updates its scales fused
+ * with the GEMM.  Besides (optionally) y = BF16(fprop result) it writes
+ *   y_q     = cast(BF16(y) * y_scale[0]) in y_fmt: exactly the bytes
+ *             fp8_quantize_tensor would produce from the BF16 y (NULL: skip;
+ *             then y_scale may be NULL too);
+ *   y_amax  = max |BF16(y)| (NaN > inf > finite), exactly what fp8_amax of
+ *             the BF16 y gives (NULL: skip);
+ * so the next layer reads the FP8 activation without another pass over y.
+ *   y_bf16  out [M][N] BF16, may be NULL when y_q is given
+ *   y_fmt   FP8 format of y_q;  y_scale  in float[1]
+ *   y_q     out uint8 [M][N];   y_amax   out float[1]
+ * At least one of y_q / y_amax must be given (else FP8_ERR_NULL; the plain
+ * call is fp8_gemm_fprop).  N % 16 == 0 (FP8_ERR_ALIGN); at most 65536
+ * 256x256 output tiles (FP8_ERR_SHAPE).  y_amax uses the workspace described
+ * under Memory.  Other rules and errors as fp8_gemm_fprop. */
+fp8_status_t fp8_gemm_fprop_fused(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,
+                                  int64_t N, int64_t K, void* y_bf16, int32_t y_fmt,
+                                  const float* y_scale, uint8_t* y_q, float* y_amax,
+                                  void* stream);
 
 /* wgrad with an FP32 result, optionally accumulated.  [snippets] forward-
  * pass snippet: the master weights are FP32, so their gradient is too;

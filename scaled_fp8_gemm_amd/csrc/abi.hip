@@ -32,10 +32,22 @@ bool have(const void* p, int64_t elems) { return p != nullptr || elems == 0; }
 bool is_block(int32_t sc) { return sc == FP8_SCALE_BLOCK_1x128 || sc == FP8_SCALE_BLOCK_128x128; }
 
 // C[rows_a][rows_b] = A[rows_a][kc] . B[rows_b][kc]^T with the operands' scales.
+// Optional fused epilogue of the BF16 mode: the next layer's FP8 copy of the
+// output (with its scale and format) and the output's amax.
+struct Fused {
+  uint8_t* cq = nullptr;
+  const float* q_scale = nullptr;
+  int q_fmt = 0;
+  float* amax = nullptr;
+};
+
 fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a,
-                  int64_t rows_b, int64_t kc, void* c, void* stream, int out = 0) {
+                  int64_t rows_b, int64_t kc, void* c, void* stream, int out = 0,
+                  const Fused& fu = Fused()) {
+  const bool fused = fu.cq != nullptr || fu.amax != nullptr;
   if (!a || !b) return FP8_ERR_NULL;
-  if (!fmt_ok(a->fmt) || !fmt_ok(b->fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!fmt_ok(a->fmt) || !fmt_ok(b->fmt) || (fu.cq && !fmt_ok(fu.q_fmt)))
+    return FP8_ERR_UNSUPPORTED;
   if (a->scaling < FP8_SCALE_TENSOR || a->scaling > FP8_SCALE_MX_1x32 ||
       b->scaling < FP8_SCALE_TENSOR || b->scaling > FP8_SCALE_MX_1x32)
     return FP8_ERR_UNSUPPORTED;
@@ -51,8 +63,11 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   if (!dims_ok(rows_a, kc) || !dims_ok(rows_b, kc)) return FP8_ERR_SHAPE;
   if (kc > kMaxContraction) return FP8_ERR_SHAPE;
   const int64_t nc = rows_a * rows_b;
-  if (!have(a->data, rows_a * kc) || !have(b->data, rows_b * kc) || !have(c, nc) ||
-      !have(a->scale_inv, nc) || !have(b->scale_inv, nc))
+  // the output may be NULL when it is empty, or in the fused call when the
+  // FP8 copy is written instead
+  const bool c_ok = have(c, nc) || fu.cq != nullptr;
+  if (!have(a->data, rows_a * kc) || !have(b->data, rows_b * kc) || !c_ok ||
+      !have(a->scale_inv, nc) || !have(b->scale_inv, nc) || (fu.cq && !fu.q_scale))
     return FP8_ERR_NULL;
   if (mode == 1) {
     if (kc % 128) return FP8_ERR_SHAPE;
@@ -60,8 +75,13 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
     if (b->scaling == FP8_SCALE_BLOCK_128x128 && rows_b % 128) return FP8_ERR_SHAPE;
   }
   if (mode == 2 && kc % 32) return FP8_ERR_SHAPE;
+  if (fused && ((rows_a + 255) / 256) * ((rows_b + 255) / 256) > fp8sg::kWorkspaceWords)
+    return FP8_ERR_SHAPE;
   if (kc % 16) return FP8_ERR_ALIGN;
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || !aligned(c, 16)) return FP8_ERR_ALIGN;
+  if (fused && (rows_b % 16 || !aligned(fu.cq, 16) || !aligned(fu.q_scale, 4) ||
+                !aligned(fu.amax, 4)))
+    return FP8_ERR_ALIGN;
   if (mode != 2 && (!aligned(a->scale_inv, 4) || !aligned(b->scale_inv, 4)))
     return FP8_ERR_ALIGN;
   GemmProblem p;
@@ -71,6 +91,11 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   p.sb = b->scale_inv;
   p.C = c;
   p.out = out;
+  p.Cq = fu.cq;
+  p.q_scale = fu.q_scale;
+  p.q_fmt = fu.q_fmt;
+  p.amax = fu.amax;
+  p.part = nullptr;
   p.M = rows_a;
   p.N = rows_b;
   p.K = kc;
@@ -218,6 +243,19 @@ fp8_status_t fp8_gemm_dgrad(const fp8_operand_t* dy, const fp8_operand_t* wT, in
 fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,
                             int64_t N, int64_t K, void* dw_bf16, void* stream) {
   return gemm(dyT, xT, N, K, M, dw_bf16, stream);
+}
+
+fp8_status_t fp8_gemm_fprop_fused(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,
+                                  int64_t N, int64_t K, void* y_bf16, int32_t y_fmt,
+                                  const float* y_scale, uint8_t* y_q, float* y_amax,
+                                  void* stream) {
+  Fused fu;
+  fu.cq = y_q;
+  fu.q_scale = y_scale;
+  fu.q_fmt = y_fmt;
+  fu.amax = y_amax;
+  if (!y_q && !y_amax) return FP8_ERR_NULL;   // use fp8_gemm_fprop
+  return gemm(x, w, M, N, K, y_bf16, stream, 0, fu);
 }
 
 fp8_status_t fp8_gemm_wgrad_f32(const fp8_operand_t* dyT, const fp8_operand_t* xT, int64_t M,

@@ -191,7 +191,11 @@ void k_gemm8(Args p) {
     __syncthreads();
   }
 
-  // Epilogue: scale (tensor mode), then BF16 / FP32 / FP32-accumulate stores.
+  // Epilogue: scale (tensor mode), then BF16 / FP32 / FP32-accumulate stores
+  // (and the fused FP8 copy and amax of the BF16 output).
+  __shared__ uint32_t red[NT / 64];
+  const float qs = p.Cq != nullptr ? *p.q_scale : 1.0f;
+  uint32_t mx = 0;
   float s = 1.0f;
   if constexpr (MODE == kTensor)
     s = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sb)[0];
@@ -204,15 +208,17 @@ void k_gemm8(Args p) {
       const int64_t n = n_base + j * 16 + 4 * g;
       if (n >= p.N) continue;
       const v4f a = acc[f][j];
-      store4(p, m, n, a[0] * s, a[1] * s, a[2] * s, a[3] * s);
+      store4(p, m, n, a[0] * s, a[1] * s, a[2] * s, a[3] * s, qs, mx);
     }
   }
+  tile_amax<NT>(p, tm, tn, mx, red);
 }
 
 template <int MODE, int FA, int FB, int BRA, int BRB>
 hipError_t run(const GemmProblem& q, hipStream_t s) {
   Args a;
   a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C; a.out = q.out;
+  a.Cq = q.Cq; a.q_scale = q.q_scale; a.q_fmt = q.q_fmt; a.part = q.part;
   a.M = q.M; a.N = q.N; a.K = q.K;
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);
@@ -235,17 +241,33 @@ hipError_t run_fmt(const GemmProblem& q, hipStream_t s) {
 
 // Blockwise needs K % 128 == 0 (checked by the ABI); MX with K % 128 != 0
 // goes to the kernel of gemm_mx_k32.hip.
-hipError_t launch_gemm(const GemmProblem& q, hipStream_t s) {
-  if (q.M == 0 || q.N == 0) return hipSuccess;
-  if (q.mode == kTensor) return w8::run_fmt<kTensor, 1, 1>(q, s);
-  if (q.mode == kMX) {
-    if (q.K % 128 != 0) return launch_gemm_mx_k32(q, s);
-    return w8::run_fmt<kMX, 1, 1>(q, s);
+hipError_t launch_gemm(const GemmProblem& q0, hipStream_t s) {
+  if (q0.M == 0 || q0.N == 0) {
+    if (q0.amax) return launch_amax_finalize(nullptr, 0, q0.amax, s);
+    return hipSuccess;
   }
-  if (q.bra == 1 && q.brb == 128) return w8::run_fmt<kBlock, 1, 128>(q, s);
-  if (q.bra == 1 && q.brb == 1) return w8::run_fmt<kBlock, 1, 1>(q, s);
-  if (q.bra == 128 && q.brb == 1) return w8::run_fmt<kBlock, 128, 1>(q, s);
-  return w8::run_fmt<kBlock, 128, 128>(q, s);
+  GemmProblem q = q0;
+  q.part = nullptr;
+  if (q.amax) {
+    hipError_t err = stream_partials(s, &q.part);
+    if (err != hipSuccess) return err;
+  }
+  hipError_t err;
+  if (q.mode == kTensor)
+    err = w8::run_fmt<kTensor, 1, 1>(q, s);
+  else if (q.mode == kMX)
+    err = q.K % 128 != 0 ? launch_gemm_mx_k32(q, s) : w8::run_fmt<kMX, 1, 1>(q, s);
+  else if (q.bra == 1 && q.brb == 128)
+    err = w8::run_fmt<kBlock, 1, 128>(q, s);
+  else if (q.bra == 1 && q.brb == 1)
+    err = w8::run_fmt<kBlock, 1, 1>(q, s);
+  else if (q.bra == 128 && q.brb == 1)
+    err = w8::run_fmt<kBlock, 128, 1>(q, s);
+  else
+    err = w8::run_fmt<kBlock, 128, 128>(q, s);
+  if (err != hipSuccess || !q.amax) return err;
+  const int T = (int)(((q.M + 255) / 256) * ((q.N + 255) / 256));
+  return launch_amax_finalize(q.part, T, q.amax, s);
 }
 
 }  // namespace fp8sg

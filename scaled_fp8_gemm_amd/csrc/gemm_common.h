@@ -34,27 +34,43 @@ struct Args {
   int64_t M, N, K;
   int tiles_m, tiles_n;
   int out;      // 0: BF16 C; 1: FP32 C; 2: FP32 C += result
+  // fused epilogue of the BF16 mode (next layer's quantisation):
+  uint8_t* Cq;          // FP8 copy of the BF16-rounded output, or NULL
+  const float* q_scale; // its scale
+  int q_fmt;            // its format
+  uint32_t* part;       // per-tile maxima of |BF16 output| (FP32 bits), or NULL
 };
 
 // Four consecutive outputs of row m, columns n .. n+3 (columns past N are
 // dropped): rounded to BF16 (nearest even), stored as FP32, or added in FP32
-// to what C holds.  16-byte / 8-byte vector stores when N % 4 == 0.
+// to what C holds.  16-byte / 8-byte vector stores when N % 4 == 0.  In the
+// BF16 mode the fused epilogue also takes mx = max(mx, |BF16 value|) (FP32
+// bits) and writes Cq = cast(BF16 value * qs) (N % 16 == 0 there); C may then
+// be NULL.
 __device__ __forceinline__ void store4(const Args& p, int64_t m, int64_t n, float a0, float a1,
-                                       float a2, float a3) {
+                                       float a2, float a3, float qs, uint32_t& mx) {
   const int64_t off = m * p.N + n;
   const bool vec = (p.N & 3) == 0;
   const float v[4] = {a0, a1, a2, a3};
   if (p.out == 0) {
-    uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
-    if (vec) {
-      uint2 o;
-      o.x = pack_bf16x2(a0, a1);
-      o.y = pack_bf16x2(a2, a3);
-      *reinterpret_cast<uint2*>(dst) = o;
-    } else {
+    const uint32_t w0 = pack_bf16x2(a0, a1), w1 = pack_bf16x2(a2, a3);
+    if (p.C != nullptr) {
+      uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
+      if (vec) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < p.N) dst[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xffffu);
+        for (int r = 0; r < 4; ++r)
+          if (n + r < p.N) dst[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xffffu);
+      }
+    }
+    if (p.part != nullptr)
+      mx = max(mx, max(max(w0 & 0x7fffu, (w0 >> 16) & 0x7fffu),
+                       max(w1 & 0x7fffu, (w1 >> 16) & 0x7fffu)) << 16);
+    if (p.Cq != nullptr) {
+      const float b0 = bf_lo(w0) * qs, b1 = bf_hi(w0) * qs, b2 = bf_lo(w1) * qs, b3 = bf_hi(w1) * qs;
+      const uint32_t q4 = p.q_fmt == kE4M3 ? cvt4<kE4M3>(b0, b1, b2, b3) : cvt4<kE5M2>(b0, b1, b2, b3);
+      *reinterpret_cast<uint32_t*>(p.Cq + off) = q4;
     }
   } else {
     float* dst = static_cast<float*>(p.C) + off;
@@ -72,6 +88,16 @@ __device__ __forceinline__ void store4(const Args& p, int64_t m, int64_t n, floa
         if (n + r < p.N) dst[r] = acc ? dst[r] + v[r] : v[r];
     }
   }
+}
+
+// End of the fused epilogue: the workgroup's largest |output| goes to
+// part[tile].  All NT threads must call it.
+template <int NT>
+__device__ __forceinline__ void tile_amax(const Args& p, int tm, int tn, uint32_t mx,
+                                          uint32_t* red) {
+  if (p.part == nullptr) return;
+  mx = block_max_u32<NT>(mx, red);
+  if (threadIdx.x == 0) p.part[tm * p.tiles_n + tn] = mx;
 }
 
 __device__ __forceinline__ int wave_id() {

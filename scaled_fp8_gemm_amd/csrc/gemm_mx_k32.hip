@@ -109,6 +109,9 @@ void k_gemm_mx_k32(Args p) {
     __syncthreads();
   }
 
+  __shared__ uint32_t red[NT / 64];
+  const float qs = p.Cq != nullptr ? *p.q_scale : 1.0f;
+  uint32_t mx = 0;
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int64_t m = m_base + f * 16 + lr;
@@ -118,15 +121,17 @@ void k_gemm_mx_k32(Args p) {
       const int64_t n = n_base + j * 16 + 4 * g;
       if (n >= p.N) continue;
       const v4f a = acc[f][j];
-      store4(p, m, n, a[0], a[1], a[2], a[3]);
+      store4(p, m, n, a[0], a[1], a[2], a[3], qs, mx);
     }
   }
+  tile_amax<NT>(p, tm, tn, mx, red);
 }
 
 template <int FA, int FB>
 hipError_t run(const GemmProblem& q, hipStream_t s) {
   Args a;
   a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C; a.out = q.out;
+  a.Cq = q.Cq; a.q_scale = q.q_scale; a.q_fmt = q.q_fmt; a.part = q.part;
   a.M = q.M; a.N = q.N; a.K = q.K;
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);
@@ -140,7 +145,6 @@ hipError_t run(const GemmProblem& q, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_mx_k32(const GemmProblem& q, hipStream_t s) {
-  if (q.M == 0 || q.N == 0) return hipSuccess;
   if (q.fa == kE4M3 && q.fb == kE4M3) return mxk32::run<kE4M3, kE4M3>(q, s);
   if (q.fa == kE5M2 && q.fb == kE4M3) return mxk32::run<kE5M2, kE4M3>(q, s);
   if (q.fa == kE4M3 && q.fb == kE5M2) return mxk32::run<kE4M3, kE5M2>(q, s);

@@ -9,6 +9,13 @@ namespace fp8sg {
 
 int device_cu_count();
 
+// Per-(device, stream) buffer of kWorkspaceWords partial maxima (FP32
+// magnitude bits), allocated on first use.
+constexpr int kWorkspaceWords = 1 << 16;
+hipError_t stream_partials(hipStream_t s, uint32_t** out);
+// amax[0] = the largest of part[0 .. n-1], as an FP32 value.
+hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s);
+
 // in: 0 = BF16 input, 1 = FP32 input
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
                        float* scale_inv, hipStream_t s, int in);
@@ -40,6 +47,12 @@ struct GemmProblem {
   int mode;
   int bra, brb;
   int out;      // 0: BF16 C; 1: FP32 C; 2: FP32 C += result
+  // fused epilogue (BF16 output mode): C may be NULL when Cq is given
+  uint8_t* Cq;          // FP8 copy of the BF16-rounded output, or NULL
+  const float* q_scale; // its scale (device float[1])
+  int q_fmt;            // its format
+  float* amax;          // amax of the BF16-rounded output, or NULL
+  uint32_t* part;       // set by launch_gemm: per-tile maxima for amax
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_mx_k32(const GemmProblem& p, hipStream_t s);

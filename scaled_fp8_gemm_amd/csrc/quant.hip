@@ -630,17 +630,20 @@ int grid_for(int64_t work_items, int per_block) {
   return (int)g;
 }
 
-// One partial-maximum buffer (kMaxPartials words) per (device, stream),
-// allocated on first use and kept until the process ends.  Work on one stream
-// runs in order, so successive calls on a stream share its buffer safely;
-// calls on different streams never share one.
+}  // namespace
+
+// One partial-maximum buffer (kWorkspaceWords words: a quantise launch uses
+// at most kMaxPartials, a GEMM with a fused amax one per output tile) per
+// (device, stream), allocated on first use and kept until the process ends.
+// Work on one stream runs in order, so successive calls on a stream share its
+// buffer safely; calls on different streams never share one.
 struct StreamBuffer {
   int dev;
   hipStream_t stream;
   uint32_t* p;
 };
-std::mutex g_partials_mu;
-std::vector<StreamBuffer> g_partials;
+static std::mutex g_partials_mu;
+static std::vector<StreamBuffer> g_partials;
 
 hipError_t stream_partials(hipStream_t s, uint32_t** out) {
   int dev = 0;
@@ -653,14 +656,12 @@ hipError_t stream_partials(hipStream_t s, uint32_t** out) {
       return hipSuccess;
     }
   void* p = nullptr;
-  err = hipMalloc(&p, kMaxPartials * sizeof(uint32_t));
+  err = hipMalloc(&p, kWorkspaceWords * sizeof(uint32_t));
   if (err != hipSuccess) return err;
   g_partials.push_back({dev, s, static_cast<uint32_t*>(p)});
   *out = static_cast<uint32_t*>(p);
   return hipSuccess;
 }
-
-}  // namespace
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -760,6 +761,12 @@ hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int
   if (part)
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,
                                                part, g, amax_out, nullptr, nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s) {
+  hipLaunchKernelGGL(k_amax_finalize<kE4M3>, dim3(1), dim3(kThreads), 0, s, part, n, amax,
+                     nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -41,7 +41,8 @@ _lib = None
 _EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_amax_f32", "fp8_quantize_tensor_f32",
             "fp8_amax_history_update", "fp8_quantize_block",
             "fp8_quantize_mx", "fp8_quantize_block_t", "fp8_quantize_mx_t", "fp8_gemm_fprop",
-            "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_gemm_wgrad_f32", "fp8_convert_f32",
+            "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_gemm_fprop_fused", "fp8_gemm_wgrad_f32",
+            "fp8_convert_f32",
             "fp8_status_string"]
 
 
@@ -68,6 +69,7 @@ def lib():
             "fp8_gemm_dgrad": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_wgrad": [vp, vp, i64, i64, i64, vp, vp],
             "fp8_gemm_wgrad_f32": [vp, vp, i64, i64, i64, vp, i32, vp],
+            "fp8_gemm_fprop_fused": [vp, vp, i64, i64, i64, vp, i32, vp, vp, vp, vp],
             "fp8_convert_f32": [vp, i64, i32, vp, vp],
         }
         for name, args in sig.items():
@@ -177,6 +179,13 @@ def fp8_gemm_dgrad(dy: Operand, wT: Operand, M, N, K, dx, stream=None):
 def fp8_gemm_wgrad(dyT: Operand, xT: Operand, M, N, K, dw, stream=None):
     _check("fp8_gemm_wgrad", lib().fp8_gemm_wgrad(ctypes.byref(dyT), ctypes.byref(xT), M, N, K,
                                                   _ptr(dw), _stream(stream)))
+
+
+def fp8_gemm_fprop_fused(x: Operand, w: Operand, M, N, K, y, y_fmt, y_scale, y_q, y_amax,
+                         stream=None):
+    _check("fp8_gemm_fprop_fused",
+           lib().fp8_gemm_fprop_fused(ctypes.byref(x), ctypes.byref(w), M, N, K, _ptr(y), y_fmt,
+                                      _ptr(y_scale), _ptr(y_q), _ptr(y_amax), _stream(stream)))
 
 
 def fp8_gemm_wgrad_f32(dyT: Operand, xT: Operand, M, N, K, dw, accumulate=False, stream=None):

@@ -139,6 +139,12 @@ def test_gemm_errors(L):
     assert g(r(t), r(t), 16, 16, (1 << 23) + 16, P, None) == SHAPE        # K > 2^23
     assert g(r(t), r(t), 16, 16, 16, PU, None) == ALIGN
     assert g(r(_op(0, 0, data=PU)), r(t), 16, 16, 16, P, None) == ALIGN
+    ff = L.fp8_gemm_fprop_fused
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, P, None, None, None) == NULL     # nothing fused
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, None, P, None, None) == NULL     # y_q without scale
+    assert ff(r(t), r(t), 16, 16, 16, P, 5, P, P, None, None) == UNSUP       # y_fmt
+    assert ff(r(t), r(t), 16, 24, 16, P, 0, P, P, None, None) == ALIGN       # N % 16
+    assert ff(r(t), r(t), 16, 16, 16, None, 0, P, None, P, None) == NULL     # amax only, no y
     wf = L.fp8_gemm_wgrad_f32
     assert wf(r(t), r(t), 16, 16, 16, P, 2, None) == UNSUP             # accumulate flag
     assert wf(r(t), r(t), 24, 16, 16, P, 0, None) == ALIGN             # M % 16

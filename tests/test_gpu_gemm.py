@@ -262,3 +262,52 @@ def test_wgrad_f32_store_and_accumulate(F, orc, scaling, M, N, K):
                    label=f"{scaling} accumulate")
     # store then accumulate agree with one FP32 add of the stored result
     assert np.array_equal(g2, (old + g1).astype(np.float32))
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "block", "mx", "mx_k32"])
+@pytest.mark.parametrize("yfmt", [E4M3, E5M2])
+def test_fprop_fused_next_layer_quantise(F, orc, scaling, yfmt):
+    """The fused epilogue writes exactly what fp8_quantize_tensor and fp8_amax
+    (pinned oracle) give for the BF16 output, with and without storing it."""
+    M, N, K = 600, 528, 384 if scaling != "mx_k32" else 352
+    rng = np.random.Generator(np.random.PCG64(51))
+    A, B = rand_codes((M, K), E4M3, 52), rand_codes((N, K), E4M3, 53)
+    if scaling == "tensor":
+        sca = scb = TENSOR
+        sa, sb = np.float32([0.013]), np.float32([0.021])
+    elif scaling == "block":
+        sca, scb = B1, B128
+        M, N = 640, 512
+        A, B = rand_codes((M, K), E4M3, 52), rand_codes((N, K), E4M3, 53)
+        sa = (rng.random((M, K // 128)) * 0.02 + 0.005).astype(np.float32)
+        sb = (rng.random((N // 128, K // 128)) * 0.02 + 0.005).astype(np.float32)
+    else:
+        sca = scb = MX
+        sa = rng.integers(118, 124, size=(M, K // 32)).astype(np.uint8)
+        sb = rng.integers(118, 124, size=(N, K // 32)).astype(np.uint8)
+        sa[7, 1] = 0xFF                                  # NaN scale: row 7 of y is NaN
+    Ad, Bd = dev_u8(A), dev_u8(B)
+    sad = dev_u8(sa) if sca == MX else dev_f32(sa)
+    sbd = dev_u8(sb) if scb == MX else dev_f32(sb)
+    oa, ob = F.operand(Ad, E4M3, sca, sad), F.operand(Bd, E4M3, scb, sbd)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(oa, ob, M, N, K, y)
+    yf = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    yq = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+    yq2 = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+    am = torch.empty(1, dtype=torch.float32, device=DEV)
+    ys = torch.tensor([0.75 if yfmt == E4M3 else 3.0], dtype=torch.float32, device=DEV)
+    F.fp8_gemm_fprop_fused(oa, ob, M, N, K, yf, yfmt, ys, yq, am)
+    F.fp8_gemm_fprop_fused(oa, ob, M, N, K, None, yfmt, ys, yq2, None)   # FP8 only
+    torch.cuda.synchronize()
+    yb = bits16(y)
+    assert np.array_equal(bits16(yf), yb)
+    wq, _, wam = orc.quantize_tensor(yb, yfmt, f32(ys)[0], want_amax=True)
+    assert np.array_equal(bytes8(yq), wq) and np.array_equal(bytes8(yq2), wq)
+    assert f32(am)[0].view(np.uint32) == np.float32(wam).view(np.uint32)
+    if scaling.startswith("mx"):
+        assert np.isnan(f32(am)[0])
+    else:
+        mode = {"tensor": 0, "block": 1}[scaling]
+        check_gemm(orc, yb, A, B, E4M3, E4M3, mode, sa, sb, 1, 128 if scaling == "block" else 1,
+                   label=f"fused {scaling}")
