@@ -22,6 +22,7 @@
  *   Memory      Every pointer argument except `stream` is device memory owned by
  *               the caller.  Tensors are dense and row-major.  The calls that
  *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out,
+ *               fp8_quantize_tensor_current,
  *               fp8_gemm_fprop_fused with y_amax) reduce through a 256 KB
  *               buffer of partial maxima that the
  *               library allocates (hipMalloc) on the first such call on each
@@ -114,6 +115,23 @@ fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fm
 fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                  void* stream);
+
+/* Per-tensor current scaling in one call: amax -> scale pair -> cast, the
+ * sequence fp8_amax + fp8_quantize_tensor with identical results
+ * ([colossal] real-time scaling takes the scale from the current tensor;
+ * [guide] three scaling algorithms).  Two launches: the amax pass, then the
+ * cast, whose workgroups each reduce the amax pass's partial maxima and
+ * derive the scale themselves (no separate finalize).
+ *   x_bf16     [rows][cols] BF16, cols % 16 == 0
+ *   q          out uint8 [rows][cols];  qT  out [cols][rows], nullable
+ *              (rows % 16 == 0)
+ *   amax       out float[1];  scale  out float[1], nullable;
+ *   scale_inv  out float[1]
+ * Uses the workspace described under Memory.  Errors as fp8_amax and
+ * fp8_quantize_tensor. */
+fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64_t cols,
+                                         int32_t fmt, uint8_t* q, uint8_t* qT, float* amax,
+                                         float* scale, float* scale_inv, void* stream);
 
 /* FP32 master-weight input.  [snippets] forward-pass snippet: the master
  * weights are FP32 and are quantised to FP8 for the GEMM.  The same calls as

@@ -156,6 +156,22 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
   return quantize_tensor_any(x_bf16, rows, cols, fmt, scale, q, qT, amax_out, stream, 0);
 }
 
+fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64_t cols,
+                                         int32_t fmt, uint8_t* q, uint8_t* qT, float* amax,
+                                         float* scale, float* scale_inv, void* stream) {
+  if (!amax || !scale_inv) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols) || !have(q, rows * cols)) return FP8_ERR_NULL;
+  if (cols % 16) return FP8_ERR_ALIGN;
+  if (qT && rows % 16) return FP8_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||
+      !aligned(amax, 4) || !aligned(scale_inv, 4) || (scale && !aligned(scale, 4)))
+    return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_quantize_current(x_bf16, rows, cols, fmt, q, qT, amax, scale,
+                                            scale_inv, st(stream), 0));
+}
+
 fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
                                      const float* scale, uint8_t* q, uint8_t* qT,
                                      float* amax_out, void* stream) {

@@ -32,13 +32,13 @@ template <> struct FmtTraits<kE5M2> {
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 // Clamp |v| to fmax when fmax < |v| <= inf; NaN and in-range values pass.
+// v_med3_f32(v, -fmax, fmax) clamps but turns NaN into a number, so NaN is
+// selected back (3 instructions).
 template <int FMT>
 __device__ __forceinline__ float saturate(float v) {
-  constexpr uint32_t mb = FmtTraits<FMT>::max_bits;
-  uint32_t u = __float_as_uint(v);
-  uint32_t a = u & 0x7fffffffu;
-  uint32_t clamped = (u & 0x80000000u) | mb;
-  return __uint_as_float((a - (mb + 1u)) < (0x7f800000u - mb) ? clamped : u);
+  constexpr float m = FmtTraits<FMT>::fmax;
+  const float r = __builtin_amdgcn_fmed3f(v, -m, m);
+  return __builtin_isnan(v) ? v : r;
 }
 
 // Four FP32 values -> four FP8 bytes, element 0 in the lowest byte.

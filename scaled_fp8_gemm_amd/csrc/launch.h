@@ -22,6 +22,10 @@ hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* sc
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                   hipStream_t s, int in);
+// amax -> scale pair -> cast in two launches (current scaling).
+hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
+                                   uint8_t* q, uint8_t* qT, float* amax, float* scale,
+                                   float* scale_inv, hipStream_t s, int in);
 hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
                                  float* scale, float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,

@@ -104,6 +104,38 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* __re
   }
 }
 
+// Current scaling inside the cast: every workgroup reduces the amax
+// launch's npart partial maxima (FP32 magnitude bits, at most kMaxPartials,
+// read from L2) and derives the same scale; workgroup 0 also writes amax,
+// scale and scale_inv.  All threads must call it.
+template <int FMT, int NT>
+__device__ __forceinline__ float scale_from_partials(const uint32_t* __restrict__ part, int npart,
+                                                     float* amax, float* scale, float* scale_inv,
+                                                     uint32_t* red) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < npart; i += NT) m = max(m, part[i]);
+  m = block_max_u32<NT>(m, red);
+  const float a = __uint_as_float(m);
+  const float s = scale_from_amax<FMT>(a);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *amax = a;
+    if (scale) *scale = s;
+    *scale_inv = 1.0f / s;
+  }
+  return s;
+}
+
+// Where a cast takes its scale from: a device float, or (current scaling)
+// the partial maxima of the amax launch just before it.
+struct ScaleSrc {
+  const float* scale;                 // NULL: current scaling
+  const uint32_t* part;
+  int npart;
+  float* amax;
+  float* scale_out;
+  float* scale_inv_out;
+};
+
 // 16 consecutive elements (16-byte aligned) times s -> 16 FP8 bytes; m takes
 // their largest magnitude.  BF16: two 16-byte loads; FP32: four.
 template <int FMT, int IN>
@@ -139,13 +171,15 @@ struct Row16 {
 // kThreads * 2 groups per workgroup step.
 template <int FMT, bool AMAX, int IN>
 __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x, int64_t n16,
-                                                   const float* __restrict__ scale_p,
-                                                   uint4* __restrict__ q,
+                                                   ScaleSrc src, uint4* __restrict__ q,
                                                    uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kThreads / 64];
   constexpr int U = 2;
   constexpr int64_t GB = 16 * (IN == kInBF16 ? 2 : 4);   // input bytes per group
-  const float s = *scale_p;
+  const float s = src.scale ? *src.scale
+                            : scale_from_partials<FMT, kThreads>(src.part, src.npart, src.amax,
+                                                                 src.scale_out,
+                                                                 src.scale_inv_out, red);
   uint32_t m = 0;
   const int64_t nchunks = (n16 + kThreads * U - 1) / (kThreads * U);
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
@@ -216,14 +250,16 @@ __device__ __forceinline__ int qt_word(int col, int a) { return col * 32 + (a ^ 
 template <int FMT, bool AMAX, int IN>
 __global__ __launch_bounds__(kThreads) void k_cast_t(const uint8_t* __restrict__ x, int64_t rows,
                                                      int64_t cols, int64_t ntx, int64_t ntiles,
-                                                     const float* __restrict__ scale_p,
-                                                     uint8_t* __restrict__ q,
+                                                     ScaleSrc src, uint8_t* __restrict__ q,
                                                      uint8_t* __restrict__ qT,
                                                      uint32_t* __restrict__ part) {
   constexpr int64_t EB = IN == kInBF16 ? 2 : 4;   // bytes per input element
   __shared__ uint32_t red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
-  const float s = *scale_p;
+  const float s = src.scale ? *src.scale
+                            : scale_from_partials<FMT, kThreads>(src.part, src.npart, src.amax,
+                                                                 src.scale_out,
+                                                                 src.scale_inv_out, red);
   const int t = threadIdx.x;
   const int a = t >> 3, c = t & 7;
   uint32_t m = 0;
@@ -298,38 +334,45 @@ __global__ __launch_bounds__(kThreads) void k_history(float* __restrict__ hist, 
 }
 
 // Blockwise 1x128: tile t covers the 128 contiguous elements [128t, 128t+128)
-// (cols % 128 == 0), handled by 16 lanes with one 16-byte load each; a lane
-// group keeps four tiles' loads in flight.
+// (cols % 128 == 0), handled by 8 lanes with two 16-byte loads each (so one
+// wave instruction covers 8 tiles and the per-tile scale division is shared
+// by 16 elements per lane); a lane group keeps two tiles' loads in flight.
 template <int FMT>
-__device__ __forceinline__ void block_1x128_tile(uint4 v, int64_t t, int sub,
-                                                 uint2* __restrict__ q,
+__device__ __forceinline__ void block_1x128_tile(uint4 v0, uint4 v1, int64_t t, int sub,
+                                                 uint4* __restrict__ q,
                                                  float* __restrict__ sinv) {
-  const uint32_t m = group_max_u32<16>(absmax8(v));
+  const uint32_t m = group_max_u32<8>(max(absmax8(v0), absmax8(v1)));
   const float s = scale_from_amax<FMT>(__uint_as_float(m << 16));
-  q[t * 16 + sub] = cast8<FMT>(v, s);
+  const uint2 lo = cast8<FMT>(v0, s), hi = cast8<FMT>(v1, s);
+  q[t * 8 + sub] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   if (sub == 0) sinv[t] = 1.0f / s;
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_block_1x128(const uint4* __restrict__ x,
                                                           int64_t ntiles,
-                                                          uint2* __restrict__ q,
+                                                          uint4* __restrict__ q,
                                                           float* __restrict__ sinv) {
-  constexpr int U = kChunkLoads, G = kThreads / 16;   // G tiles per load step
-  const int sub = threadIdx.x & 15;
+  constexpr int U = kChunkLoads / 2, G = kThreads / 8;   // G tiles per load step
+  const int sub = threadIdx.x & 7;
   const int64_t nchunks = (ntiles + G * U - 1) / (G * U);
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-    const int64_t t = c * (G * U) + (threadIdx.x >> 4);
+    const int64_t t = c * (G * U) + (threadIdx.x >> 3);
     if (t + (U - 1) * G < ntiles) {
-      uint4 v[U];
+      uint4 v[U][2];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[(t + u * G) * 16 + sub]);
+      for (int u = 0; u < U; ++u) {
+        v[u][0] = ld_stream(&x[(t + u * G) * 16 + 2 * sub]);
+        v[u][1] = ld_stream(&x[(t + u * G) * 16 + 2 * sub + 1]);
+      }
 #pragma unroll
-      for (int u = 0; u < U; ++u) block_1x128_tile<FMT>(v[u], t + u * G, sub, q, sinv);
+      for (int u = 0; u < U; ++u) block_1x128_tile<FMT>(v[u][0], v[u][1], t + u * G, sub, q, sinv);
     } else {
       for (int u = 0; u < U; ++u)
         if (t + u * G < ntiles)
-          block_1x128_tile<FMT>(ld_stream(&x[(t + u * G) * 16 + sub]), t + u * G, sub, q, sinv);
+          block_1x128_tile<FMT>(ld_stream(&x[(t + u * G) * 16 + 2 * sub]),
+                                ld_stream(&x[(t + u * G) * 16 + 2 * sub + 1]), t + u * G, sub,
+                                q, sinv);
     }
   }
 }
@@ -713,7 +756,7 @@ hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* sc
 }
 
 template <int IN>
-static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, const float* scale,
+static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
                          uint8_t* q, uint8_t* qT, uint32_t* part, int& g, hipStream_t s) {
   const int64_t n = rows * cols;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
@@ -724,20 +767,20 @@ static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, con
     FP8SG_FMT_DISPATCH(fmt, {
       if (part)
         hipLaunchKernelGGL((k_cast_t<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, rows, cols,
-                           ntx, ntiles, scale, q, qT, part);
+                           ntx, ntiles, src, q, qT, part);
       else
         hipLaunchKernelGGL((k_cast_t<F, false, IN>), dim3(g), dim3(kThreads), 0, s, xb, rows,
-                           cols, ntx, ntiles, scale, q, qT, part);
+                           cols, ntx, ntiles, src, q, qT, part);
     });
   } else {
     const int64_t n16 = n / 16;
     g = grid_for(n16, kThreads * 2);
     FP8SG_FMT_DISPATCH(fmt, {
       if (part)
-        hipLaunchKernelGGL((k_cast<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, scale,
+        hipLaunchKernelGGL((k_cast<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, src,
                            reinterpret_cast<uint4*>(q), part);
       else
-        hipLaunchKernelGGL((k_cast<F, false, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, scale,
+        hipLaunchKernelGGL((k_cast<F, false, IN>), dim3(g), dim3(kThreads), 0, s, xb, n16, src,
                            reinterpret_cast<uint4*>(q), part);
     });
   }
@@ -751,16 +794,47 @@ hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int
     hipError_t err = stream_partials(s, &part);
     if (err != hipSuccess) return err;
   }
+  ScaleSrc src{scale, nullptr, 0, nullptr, nullptr, nullptr};
   int g = 0;
   if (rows * cols > 0) {
     if (in == kInBF16)
-      cast_kernels<kInBF16>(x, rows, cols, fmt, scale, q, qT, part, g, s);
+      cast_kernels<kInBF16>(x, rows, cols, fmt, src, q, qT, part, g, s);
     else
-      cast_kernels<kInF32>(x, rows, cols, fmt, scale, q, qT, part, g, s);
+      cast_kernels<kInF32>(x, rows, cols, fmt, src, q, qT, part, g, s);
   }
   if (part)
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_amax_finalize<F>, dim3(1), dim3(kThreads), 0, s,
                                                part, g, amax_out, nullptr, nullptr));
+  return hipGetLastError();
+}
+
+// Current scaling: the amax launch writes partials, the cast reduces them
+// itself (no separate finalize launch).
+hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
+                                   uint8_t* q, uint8_t* qT, float* amax, float* scale,
+                                   float* scale_inv, hipStream_t s, int in) {
+  const int64_t n = rows * cols;
+  if (n == 0) return launch_amax(x, 0, fmt, amax, scale, scale_inv, s, in);
+  uint32_t* part = nullptr;
+  hipError_t err = stream_partials(s, &part);
+  if (err != hipSuccess) return err;
+  const int per = in == kInBF16 ? 8 : 4;
+  const int64_t nvec = n / per;
+  const int ntail = (int)(n - nvec * per);
+  const void* tail = static_cast<const uint8_t*>(x) + nvec * 16;
+  const int ga = grid_for(nvec > 0 ? nvec : 1, kThreads * kChunkLoads);
+  if (in == kInBF16)
+    hipLaunchKernelGGL(k_amax<kInBF16>, dim3(ga), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), nvec, tail, ntail, part);
+  else
+    hipLaunchKernelGGL(k_amax<kInF32>, dim3(ga), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), nvec, tail, ntail, part);
+  ScaleSrc src{nullptr, part, ga, amax, scale, scale_inv};
+  int g = 0;
+  if (in == kInBF16)
+    cast_kernels<kInBF16>(x, rows, cols, fmt, src, q, qT, nullptr, g, s);
+  else
+    cast_kernels<kInF32>(x, rows, cols, fmt, src, q, qT, nullptr, g, s);
   return hipGetLastError();
 }
 
@@ -782,10 +856,10 @@ hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int 
   if (rows * cols == 0) return hipSuccess;
   if (br == 1) {
     const int64_t ntiles = rows * (cols / 128);
-    const int g = grid_for(ntiles, (kThreads / 16) * kChunkLoads);
+    const int g = grid_for(ntiles, (kThreads / 8) * (kChunkLoads / 2));
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_1x128<F>, dim3(g), dim3(kThreads), 0, s,
                                                static_cast<const uint4*>(x), ntiles,
-                                               reinterpret_cast<uint2*>(q), scale_inv));
+                                               reinterpret_cast<uint4*>(q), scale_inv));
   } else {
     dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_128<F>, grid, dim3(kThreads), 0, s,

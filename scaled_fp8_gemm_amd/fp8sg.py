@@ -38,7 +38,8 @@ class Operand(ctypes.Structure):
 
 
 _lib = None
-_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_amax_f32", "fp8_quantize_tensor_f32",
+_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_quantize_tensor_current", "fp8_amax_f32",
+            "fp8_quantize_tensor_f32",
             "fp8_amax_history_update", "fp8_quantize_block",
             "fp8_quantize_mx", "fp8_quantize_block_t", "fp8_quantize_mx_t", "fp8_gemm_fprop",
             "fp8_gemm_dgrad", "fp8_gemm_wgrad", "fp8_gemm_fprop_fused", "fp8_gemm_wgrad_f32",
@@ -59,6 +60,7 @@ def lib():
             "fp8_amax": [vp, i64, i64, i32, vp, vp, vp, vp],
             "fp8_quantize_tensor": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_amax_f32": [vp, i64, i64, i32, vp, vp, vp, vp],
+            "fp8_quantize_tensor_current": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
             "fp8_quantize_tensor_f32": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_amax_history_update": [vp, i32, i64, vp, i32, vp, vp, vp],
             "fp8_quantize_block": [vp, i64, i64, i32, i32, i32, vp, vp, vp],
@@ -113,6 +115,14 @@ def fp8_quantize_tensor(x, fmt, scale, q, qT=None, amax_out=None, stream=None):
     _check("fp8_quantize_tensor",
            lib().fp8_quantize_tensor(_ptr(x), rows, cols, fmt, _ptr(scale), _ptr(q), _ptr(qT),
                                      _ptr(amax_out), _stream(stream)))
+
+
+def fp8_quantize_tensor_current(x, fmt, q, qT, amax, scale, scale_inv, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_quantize_tensor_current",
+           lib().fp8_quantize_tensor_current(_ptr(x), rows, cols, fmt, _ptr(q), _ptr(qT),
+                                             _ptr(amax), _ptr(scale), _ptr(scale_inv),
+                                             _stream(stream)))
 
 
 def fp8_amax_f32(x, fmt, amax, scale=None, scale_inv=None, stream=None):

@@ -84,6 +84,15 @@ def test_block_and_mx_errors(L):
     assert m(PU, 4, 64, 0, P, P, None) == ALIGN
 
 
+def test_quantize_current_errors(L):
+    c = L.fp8_quantize_tensor_current
+    assert c(P, 4, 16, 0, P, None, None, None, P, None) == NULL        # amax
+    assert c(P, 4, 16, 0, P, None, P, None, None, None) == NULL        # scale_inv
+    assert c(P, 4, 24, 0, P, None, P, None, P, None) == ALIGN          # cols % 16
+    assert c(P, 8, 16, 0, P, P, P, None, P, None) == ALIGN             # qT rows % 16
+    assert c(P, 4, 16, 2, P, None, P, None, P, None) == UNSUP
+
+
 def test_f32_input_errors(L):
     a = L.fp8_amax_f32
     assert a(P, 4, 16, 0, None, None, None, None) == NULL

@@ -153,6 +153,32 @@ def test_quantize_mx(F, orc, shape, fmt):
     assert np.array_equal(bytes8(q), wq)
 
 
+@pytest.mark.parametrize("shape,transposed", [((0, 16), False), ((1, 16), False),
+                                              ((37, 48), False), ((272, 384), True),
+                                              ((4112, 8208), False), ((4112, 8208), True)])
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_tensor_current(F, orc, shape, transposed, fmt):
+    """One-call current scaling = fp8_amax + fp8_quantize_tensor, bit for bit,
+    and the oracle's amax / scale rule / cast."""
+    x = rand_bits(shape, 101 + shape[1], 2.0, specials=True)
+    xd = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    R, C = shape
+    q = empty_dev(shape, torch.uint8)
+    qT = empty_dev((C, R), torch.uint8) if transposed else None
+    am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+    F.fp8_quantize_tensor_current(xd, fmt, q, qT, am, s, si)
+    wa = orc.amax(x) if x.size else 0.0
+    ws, wsi = orc.scale_from_amax(wa, fmt)
+    assert f32(am)[0].view(np.uint32) == np.float32(wa).view(np.uint32)
+    assert f32(s)[0] == ws and f32(si)[0] == wsi
+    if x.size == 0:
+        return
+    wq, wqT, _ = orc.quantize_tensor(x, fmt, ws, transposed=transposed)
+    assert np.array_equal(bytes8(q), wq)
+    if transposed:
+        assert np.array_equal(bytes8(qT), wqT)
+
+
 def rand_f32(shape, seed, scale=1.0):
     """FP32 values with a wide magnitude range and a few specials."""
     rng = np.random.Generator(np.random.PCG64(seed))
