@@ -176,18 +176,31 @@ __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x
   __shared__ uint32_t red[kThreads / 64];
   constexpr int U = 2;
   constexpr int64_t GB = 16 * (IN == kInBF16 ? 2 : 4);   // input bytes per group
+  const int64_t nchunks = (n16 + kThreads * U - 1) / (kThreads * U);
+  // The first chunk's loads go out before the scale is known (with current
+  // scaling its reduction would otherwise sit in front of every workgroup).
+  Row16<FMT, IN> r[U];
+  bool first_loaded = false;
+  if ((int64_t)blockIdx.x < nchunks) {
+    const int64_t i = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+    if (i + (U - 1) * kThreads < n16) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u].load(x + (i + u * kThreads) * GB);
+      first_loaded = true;
+    }
+  }
   const float s = src.scale ? *src.scale
                             : scale_from_partials<FMT, kThreads>(src.part, src.npart, src.amax,
                                                                  src.scale_out,
                                                                  src.scale_inv_out, red);
   uint32_t m = 0;
-  const int64_t nchunks = (n16 + kThreads * U - 1) / (kThreads * U);
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     const int64_t i = c * (kThreads * U) + threadIdx.x;
     if (i + (U - 1) * kThreads < n16) {
-      Row16<FMT, IN> r[U];
+      if (!(first_loaded && c == (int64_t)blockIdx.x)) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) r[u].load(x + (i + u * kThreads) * GB);
+        for (int u = 0; u < U; ++u) r[u].load(x + (i + u * kThreads) * GB);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (AMAX) m = max(m, r[u].absmax());
