@@ -199,6 +199,38 @@ void k_gemm8(Args p) {
   float s = 1.0f;
   if constexpr (MODE == kTensor)
     s = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sb)[0];
+  static_assert(BN * 2 == 512 && 2 * BM * BK == 128 * 512 && 2 * BN * BK == 128 * 512,
+                "the output tile is staged as 256 rows of 512 bytes over lA and lB");
+  if (p.out == 0 && p.Cq == nullptr && p.part == nullptr && (p.N & 7) == 0) {
+    // Plain BF16 output: the tile goes through LDS (free after the main loop's
+    // last barrier) so that global stores cover whole rows, 16 bytes per lane,
+    // instead of 32-byte pieces of 16 rows per instruction.  256 rows of 512
+    // bytes: rows 0-127 over lA, 128-255 over lB; 16-byte chunks XOR-swizzled
+    // by row (two lanes per bank at most when writing, none when reading).
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const v4f a = acc[f][j];
+        const int r = wm * WM + f * 16 + lr, c = wn * WN + j * 16 + 4 * g;
+        uint8_t* row = r < 128 ? &lA[0][0] + r * 512 : &lB[0][0] + (r - 128) * 512;
+        *reinterpret_cast<uint2*>(row + (((c >> 3) ^ (r & 31)) << 4) + ((c >> 2) & 1) * 8) =
+            make_uint2(pack_bf16x2(a[0] * s, a[1] * s), pack_bf16x2(a[2] * s, a[3] * s));
+      }
+    __syncthreads();
+    const int t = threadIdx.x, ch = t & 31;
+#pragma unroll 4
+    for (int k = 0; k < BM / 16; ++k) {
+      const int r = k * 16 + (t >> 5);
+      const int64_t m = m0 + r, n = n0 + ch * 8;
+      if (m < p.M && n < p.N) {
+        const uint8_t* row = r < 128 ? &lA[0][0] + r * 512 : &lB[0][0] + (r - 128) * 512;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.C) + m * p.N + n) =
+            *reinterpret_cast<const uint4*>(row + ((ch ^ (r & 31)) << 4));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int64_t m = m_base + f * 16 + lr;
