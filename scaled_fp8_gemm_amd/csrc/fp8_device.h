@@ -33,27 +33,32 @@ constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 // Clamp |v| to fmax when fmax < |v| <= inf; NaN and in-range values pass.
 // v_med3_f32(v, -fmax, fmax) clamps but turns NaN into a number, so NaN is
-// selected back (3 instructions).
-template <int FMT>
+// selected back (3 instructions).  NANS = false is for callers that know v is
+// not NaN: the clamp alone (1 instruction).
+template <int FMT, bool NANS = true>
 __device__ __forceinline__ float saturate(float v) {
   constexpr float m = FmtTraits<FMT>::fmax;
   const float r = __builtin_amdgcn_fmed3f(v, -m, m);
+  if constexpr (!NANS) return r;
   return __builtin_isnan(v) ? v : r;
 }
 
 // Four FP32 values -> four FP8 bytes, element 0 in the lowest byte.
-template <int FMT>
+template <int FMT, bool NANS = true>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  a = saturate<FMT>(a);
-  b = saturate<FMT>(b);
-  c = saturate<FMT>(c);
-  d = saturate<FMT>(d);
-  int w;
+  a = saturate<FMT, NANS>(a);
+  b = saturate<FMT, NANS>(b);
+  c = saturate<FMT, NANS>(c);
+  d = saturate<FMT, NANS>(d);
+  // The first conversion writes the low half and the second the high half,
+  // so the initial contents of the word do not matter: it starts as a's bits
+  // (a register that dies here) rather than a zero that needs a move.
+  int w = __float_as_int(a);
   if constexpr (FMT == kE4M3) {
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   } else {
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, w, false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
   }
   return (uint32_t)w;
@@ -82,11 +87,11 @@ __device__ __forceinline__ uint32_t absmax8(uint4 v) {
 }
 
 // Eight BF16 values (one 16-byte load) times `s` -> eight FP8 bytes.
-template <int FMT>
+template <int FMT, bool NANS = true>
 __device__ __forceinline__ uint2 cast8(uint4 v, float s) {
   uint2 r;
-  r.x = cvt4<FMT>(bf_lo(v.x) * s, bf_hi(v.x) * s, bf_lo(v.y) * s, bf_hi(v.y) * s);
-  r.y = cvt4<FMT>(bf_lo(v.z) * s, bf_hi(v.z) * s, bf_lo(v.w) * s, bf_hi(v.w) * s);
+  r.x = cvt4<FMT, NANS>(bf_lo(v.x) * s, bf_hi(v.x) * s, bf_lo(v.y) * s, bf_hi(v.y) * s);
+  r.y = cvt4<FMT, NANS>(bf_lo(v.z) * s, bf_hi(v.z) * s, bf_lo(v.w) * s, bf_hi(v.w) * s);
   return r;
 }
 

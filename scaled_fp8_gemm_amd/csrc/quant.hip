@@ -492,26 +492,139 @@ __global__ __launch_bounds__(kThreads) void k_mx(const uint4* __restrict__ x, in
 //   kTBlock1   q: 1x128 blocks per row; qT: per column, 128-row blocks
 //   kTBlock128 one scale per 128x128 block; qT is the transpose of q
 //   kTMX       q: 1x32 E8M0 blocks per row; qT: per column, 32-row blocks
-// A 256-thread workgroup handles a 128 x 128 tile as k_cast_t does (thread t:
-// rows 4a .. 4a+3, a = t / 8, columns 16c .. 16c+15, c = t % 8): row maxima
-// reduce over the 8 lanes of a row (1x128) or 2 lanes (1x32); column maxima
-// over the thread's 4 rows, then over the 8 lanes of a column in the wave
-// (32 rows: one MX block), then across the 4 waves through LDS (128 rows).
-// The column-scaled bytes go through the LDS transpose of k_cast_t.
+// A 256-thread workgroup handles a 128 x 128 tile; thread t owns the 8 x 8
+// block of rows 8r .. 8r+7 (r = t / 16) and columns 8c .. 8c+7 (c = t % 16),
+// one 16-byte load per row.  So a wave holds 32 whole rows, a 16-lane row of
+// the wave holds 8 whole tile rows (one 1x128 block each), a lane quad 8 rows
+// of one 1x32 block, and the 4 lanes c, c+16, c+32, c+48 one 32-row column
+// block.  BF16 magnitudes are reduced two at a time (v_pk_max_u16): per
+// thread row and column maxima, then row maxima across the quad (MX) or the
+// 16-lane row (1x128) with DPP, column maxima across the wave with the
+// gfx950 row / half swaps (v_permlane16_swap, v_permlane32_swap), and for
+// 128-row column blocks across the 4 waves through LDS.  Each scale is
+// computed by one lane and broadcast (DPP in a quad, ds_swizzle in a 16-lane
+// row, the swaps across rows), so a thread performs 2-6 scale computations
+// instead of 16.  The column-wise cast builds each FP8 word from 4 rows of
+// one column, so the transpose costs nothing: a thread stores 8 bytes (rows
+// 8r .. 8r+7) of each of its 8 qT rows.  A wave whose elements hold no NaN
+// saturates with the clamp alone.
 enum : int { kTBlock1 = 0, kTBlock128 = 1, kTMX = 2 };
 
-// Element j (0..15) of a thread's row held as two 16-byte loads.
-__device__ __forceinline__ float row_elem(const uint4 (&v)[2], int j) {
-  const uint4 h = v[j >> 3];
-  const int wd = (j & 7) >> 1;
-  const uint32_t w = wd == 0 ? h.x : wd == 1 ? h.y : wd == 2 ? h.z : h.w;
-  return (j & 1) ? bf_hi(w) : bf_lo(w);
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+// Per-half maximum of two pairs of 16-bit magnitudes.
+__device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
 }
-__device__ __forceinline__ uint32_t row_mag(const uint4 (&v)[2], int j) {
-  const uint4 h = v[j >> 3];
-  const int wd = (j & 7) >> 1;
-  const uint32_t w = wd == 0 ? h.x : wd == 1 ? h.y : wd == 2 ? h.z : h.w;
-  return ((j & 1) ? (w >> 16) : w) & 0x7fffu;
+// DPP lane move inside rows of 16 lanes (quad_perm / row_ror controls).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (one column block of a wave).
+__device__ __forceinline__ uint32_t rows_max(uint32_t v) {
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = pmax16(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return pmax16(b[0], b[1]);
+}
+// Every lane gets the values x, y of all four 16-lane rows of the wave:
+// out[2r] = x of row r, out[2r + 1] = y of row r (row r = lanes 16r .. 16r+15).
+__device__ __forceinline__ void rows_gather(float x, float y, float (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t v = __float_as_uint(e ? y : x);
+    auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);    // rows 0|2, 1|3
+    auto b0 = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);  // rows 0, 2
+    auto b1 = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);  // rows 1, 3
+    out[0 + e] = __uint_as_float(b0[0]);
+    out[4 + e] = __uint_as_float(b0[1]);
+    out[2 + e] = __uint_as_float(b1[0]);
+    out[6 + e] = __uint_as_float(b1[1]);
+  }
+}
+// out[i] = x of lane i of the lane's 16-lane row, i < 8 (ds_swizzle in
+// bitmask mode: source lane = (lane & 0x10) | i within each 32-lane half).
+template <int I>
+__device__ __forceinline__ float swz_lane(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (I << 5)));
+}
+__device__ __forceinline__ void row_bcast8(float x, float (&out)[8]) {
+  out[0] = swz_lane<0>(x); out[1] = swz_lane<1>(x); out[2] = swz_lane<2>(x); out[3] = swz_lane<3>(x);
+  out[4] = swz_lane<4>(x); out[5] = swz_lane<5>(x); out[6] = swz_lane<6>(x); out[7] = swz_lane<7>(x);
+}
+__device__ __forceinline__ uint32_t pick4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          int i) {
+  const uint32_t lo = (i & 1) ? a1 : a0, hi = (i & 1) ? a3 : a2;
+  return (i & 2) ? hi : lo;
+}
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// LDS copy of a qT tile: 128 qT rows (x's columns) of 32 words; the 8 bytes
+// of rows 8r .. 8r+7 of column col are words 2r, 2r+1, stored at
+// col*32 + (2r ^ 4*((col >> 3) & 7)), which spreads a wave's 8-byte writes
+// over all banks and keeps every aligned group of 4 words whole for the
+// 16-byte reads.
+__device__ __forceinline__ int qt8_word(int col, int w2) { return col * 32 + (w2 ^ (((col >> 3) & 7) << 2)); }
+
+// The two casts of a thread's 8 x 8 block: row i of q with scale sr[i]
+// (skipped when q is null), column j of qT with scale sc[j] into the LDS
+// qT tile T.
+template <int FMT, bool NANS>
+__device__ __forceinline__ void quant_t_emit(const uint4 (&v)[8], const float (&sr)[8],
+                                             const float (&sc)[8], uint8_t* qrow, int64_t cols,
+                                             uint32_t* T, int tc, int tr) {
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[i][2 * k] = bf_lo(word_of(v[i], k));
+      f[i][2 * k + 1] = bf_hi(word_of(v[i], k));
+    }
+  if (qrow != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = sr[i];
+      *reinterpret_cast<uint2*>(qrow + i * cols) =
+          make_uint2(cvt4<FMT, NANS>(f[i][0] * s, f[i][1] * s, f[i][2] * s, f[i][3] * s),
+                     cvt4<FMT, NANS>(f[i][4] * s, f[i][5] * s, f[i][6] * s, f[i][7] * s));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float s = sc[j];
+    *reinterpret_cast<uint2*>(&T[qt8_word(8 * tc + j, 2 * tr)]) =
+        make_uint2(cvt4<FMT, NANS>(f[0][j] * s, f[1][j] * s, f[2][j] * s, f[3][j] * s),
+                   cvt4<FMT, NANS>(f[4][j] * s, f[5][j] * s, f[6][j] * s, f[7][j] * s));
+  }
+}
+
+// The same with one scale for the whole block (128x128 blocks): qT's bytes
+// are q's, transposed 4 x 4 bytes at a time in registers.
+template <int FMT, bool NANS>
+__device__ __forceinline__ void quant_t_emit_uniform(const uint4 (&v)[8], float s, uint8_t* qrow,
+                                                     int64_t cols, uint32_t* T, int tc, int tr) {
+  uint32_t b[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint2 r = cast8<FMT, NANS>(v[i], s);
+    b[i][0] = r.x;
+    b[i][1] = r.y;
+    if (qrow != nullptr) *reinterpret_cast<uint2*>(qrow + i * cols) = r;
+  }
+  uint32_t lo[8], hi[8];   // column j: rows 0..3 in lo[j], rows 4..7 in hi[j]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    transpose4x4(b[0][h], b[1][h], b[2][h], b[3][h], &lo[4 * h]);
+    transpose4x4(b[4][h], b[5][h], b[6][h], b[7][h], &hi[4 * h]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint2*>(&T[qt8_word(8 * tc + j, 2 * tr)]) = make_uint2(lo[j], hi[j]);
 }
 
 template <int FMT, int KIND>
@@ -522,140 +635,172 @@ __global__ __launch_bounds__(kThreads) void k_quant_t(const uint16_t* __restrict
                                                       uint8_t* __restrict__ qT,
                                                       void* __restrict__ sqT) {
   constexpr int RB = KIND == kTMX ? 32 : 128;   // block length along a row / a column
+  constexpr uint32_t kMag = 0x7fff7fffu;
   __shared__ uint32_t red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint4 cmax[2][4][16];
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
-  __shared__ __attribute__((aligned(16))) uint32_t cmax[KIND == kTBlock1 ? 2 : 1][4][128];
-  const int t = threadIdx.x;
-  const int a = t >> 3, c = t & 7, w = t >> 6, lane = t & 63;
+  __shared__ uint32_t colb[KIND == kTMX ? 2 : 1][128];   // MX: a column's 4 E8M0 bytes
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int tc = t & 15, tr = t >> 4, qd = lane >> 4;   // qd: the lane's 16-lane row
   const int64_t row_blocks = cols / RB, col_blocks = rows / RB;
   int buf = 0;
   for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x, buf ^= 1) {
     const int64_t r0 = (tt / ntx) * 128, c0 = (tt % ntx) * 128;
     const int rv = (int)min<int64_t>(128, rows - r0), cv = (int)min<int64_t>(128, cols - c0);
-    const bool valid = 4 * a < rv && 16 * c < cv;
-    uint4 v[4][2];
+    // rv, cv are multiples of 32 (only MX tiles can be partial): a wave's
+    // rows and a quad's columns are valid or invalid together, so the
+    // reductions below never mix a valid lane with an invalid one.  Invalid
+    // lanes read the tile's first 8 x 8 block instead (in bounds) and store
+    // nothing.
+    const bool valid = 8 * tr < rv && 8 * tc < cv;
+    const int64_t row = r0 + 8 * tr, col = c0 + 8 * tc;
+    const uint16_t* src = valid ? x + row * cols + col : x + r0 * cols + c0;
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (valid) {
-        const uint16_t* src = x + (r0 + 4 * a + i) * cols + c0 + 16 * c;
-        v[i][0] = ld_stream(src);
-        v[i][1] = ld_stream(src + 8);
-      } else {
-        v[i][0] = v[i][1] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    uint32_t rm[4], cm[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rm[i] = max(absmax8(v[i][0]), absmax8(v[i][1]));
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      cm[j] = max(max(row_mag(v[0], j), row_mag(v[1], j)), max(row_mag(v[2], j), row_mag(v[3], j)));
+    for (int i = 0; i < 8; ++i) v[i] = ld_stream(src + i * cols);
 
-    // ---- row-wise copy
-    float st = 1.0f;   // kTBlock128: the tile's scale (rows and columns alike)
+    // P[i]: row i's magnitude maxima (even, odd columns); C[k]: columns 2k, 2k+1
+    uint32_t P[8], C[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a[k] = word_of(v[i], k) & kMag;
+        C[k] = i == 0 ? a[k] : pmax16(C[k], a[k]);
+      }
+      P[i] = pmax16(pmax16(a[0], a[1]), pmax16(a[2], a[3]));
+    }
+    const uint32_t cl = pmax16(pmax16(C[0], C[1]), pmax16(C[2], C[3]));
+    const uint32_t mloc = max(cl & 0xffffu, cl >> 16);
+    const bool nan_wave = __builtin_amdgcn_ballot_w64(mloc > 0x7f80u) != 0;
+
+    float sr[8], sc[8];
     if constexpr (KIND == kTBlock128) {
-      const uint32_t m = block_max_u32<kThreads>(max(max(rm[0], rm[1]), max(rm[2], rm[3])), red);
-      st = scale_from_amax<FMT>(__uint_as_float(m << 16));
-    }
-    if (q != nullptr) {
+      const uint32_t m = block_max_u32<kThreads>(mloc, red);
+      const float st = scale_from_amax<FMT>(__uint_as_float(m << 16));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sr;
-        uint32_t byte = 0;
-        if constexpr (KIND == kTBlock1) sr = scale_from_amax<FMT>(__uint_as_float(group_max_u32<8>(rm[i]) << 16));
-        else if constexpr (KIND == kTMX) sr = mx_scale<FMT>(group_max_u32<2>(rm[i]), byte);
-        else sr = st;
-        if (valid) {
-          const uint2 lo = cast8<FMT>(v[i][0], sr), hi = cast8<FMT>(v[i][1], sr);
-          const int64_t row = r0 + 4 * a + i;
-          *reinterpret_cast<uint4*>(q + row * cols + c0 + 16 * c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          if constexpr (KIND == kTBlock1) {
-            if (c == 0) static_cast<float*>(sq)[row * row_blocks + c0 / 128] = 1.0f / sr;
-          } else if constexpr (KIND == kTMX) {
-            if ((c & 1) == 0) static_cast<uint8_t*>(sq)[row * row_blocks + (c0 + 16 * c) / 32] = (uint8_t)byte;
-          }
+      for (int i = 0; i < 8; ++i) sr[i] = sc[i] = st;
+      if (t == 0) {
+        const float inv = 1.0f / st;
+        if (q != nullptr) static_cast<float*>(sq)[(r0 / 128) * row_blocks + c0 / 128] = inv;
+        static_cast<float*>(sqT)[(c0 / 128) * col_blocks + r0 / 128] = inv;
+      }
+    } else {
+      // R[k]: maxima of rows 2k (low half) and 2k+1 (high half)
+      uint32_t R[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        R[k] = pmax16(__builtin_amdgcn_perm(P[2 * k + 1], P[2 * k], 0x05040100u),
+                      __builtin_amdgcn_perm(P[2 * k + 1], P[2 * k], 0x07060302u));
+        R[k] = pmax16(R[k], dpp<kDppXor1>(R[k]));
+        R[k] = pmax16(R[k], dpp<kDppXor2>(R[k]));
+        if constexpr (KIND == kTBlock1) {
+          R[k] = pmax16(R[k], dpp<kDppRor4>(R[k]));
+          R[k] = pmax16(R[k], dpp<kDppRor8>(R[k]));
         }
       }
-      if constexpr (KIND == kTBlock128)
-        if (t == 0) static_cast<float*>(sq)[(r0 / 128) * row_blocks + c0 / 128] = 1.0f / st;
-    }
-
-    // ---- column scales
-    float sc[16];
-    uint32_t cbyte[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if constexpr (KIND == kTBlock128) {
-        sc[j] = st;
-      } else {
-        uint32_t m = cm[j];
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-        if constexpr (KIND == kTMX) {
-          sc[j] = mx_scale<FMT>(m, cbyte[j]);
-        } else {
-          cm[j] = m;   // this wave's 32 rows
-        }
-      }
-    }
-    if constexpr (KIND == kTBlock1) {
-      if (lane < 8) {
-#pragma unroll
-        for (int j = 0; j < 16; j += 4)
-          *reinterpret_cast<uint4*>(&cmax[buf][w][16 * c + j]) = make_uint4(cm[j], cm[j + 1], cm[j + 2], cm[j + 3]);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        uint4 m4 = *reinterpret_cast<const uint4*>(&cmax[buf][0][16 * c + j]);
+      for (int k = 0; k < 4; ++k) C[k] = rows_max(C[k]);   // this wave's 32 rows
+      if constexpr (KIND == kTBlock1) {
+        if (lane < 16) cmax[buf][w][tc] = make_uint4(C[0], C[1], C[2], C[3]);
+        __syncthreads();
+        uint4 m4 = cmax[buf][0][tc];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) {
-          const uint4 o = *reinterpret_cast<const uint4*>(&cmax[buf][ww][16 * c + j]);
-          m4.x = max(m4.x, o.x); m4.y = max(m4.y, o.y); m4.z = max(m4.z, o.z); m4.w = max(m4.w, o.w);
+          const uint4 o = cmax[buf][ww][tc];
+          m4 = make_uint4(pmax16(m4.x, o.x), pmax16(m4.y, o.y), pmax16(m4.z, o.z),
+                          pmax16(m4.w, o.w));
         }
-        sc[j] = scale_from_amax<FMT>(__uint_as_float(m4.x << 16));
-        sc[j + 1] = scale_from_amax<FMT>(__uint_as_float(m4.y << 16));
-        sc[j + 2] = scale_from_amax<FMT>(__uint_as_float(m4.z << 16));
-        sc[j + 3] = scale_from_amax<FMT>(__uint_as_float(m4.w << 16));
+        C[0] = m4.x; C[1] = m4.y; C[2] = m4.z; C[3] = m4.w;
+        // row scales: lane c of a 16-lane row computes tile row 8r + (c & 7)
+        const int ri = tc & 7;
+        const uint32_t pr = pick4(R[0], R[1], R[2], R[3], ri >> 1);
+        const float s = scale_from_amax<FMT>(__uint_as_float(((ri & 1) ? pr >> 16 : pr & 0xffffu) << 16));
+        row_bcast8(s, sr);
+        if (q != nullptr && valid && tc < 8)
+          static_cast<float*>(sq)[(row + tc) * row_blocks + c0 / 128] = 1.0f / s;
+        // column scales: lanes of 16-lane row qd compute columns 2qd, 2qd+1
+        const uint32_t pc = pick4(C[0], C[1], C[2], C[3], qd);
+        const float s0 = scale_from_amax<FMT>(__uint_as_float(pc << 16));
+        const float s1 = scale_from_amax<FMT>(__uint_as_float(pc & 0xffff0000u));
+        rows_gather(s0, s1, sc);
+        if (w == 0 && valid) {
+          float* o = static_cast<float*>(sqT) + (col + 2 * qd) * col_blocks + r0 / 128;
+          o[0] = 1.0f / s0;
+          o[col_blocks] = 1.0f / s1;
+        }
+      } else {
+        // MX rows: lane b of a quad computes rows 2b, 2b+1 of its 32-column block
+        const int b = tc & 3;
+        const uint32_t pr = pick4(R[0], R[1], R[2], R[3], b);
+        uint32_t by0, by1;
+        const float s0 = mx_scale<FMT>(pr & 0xffffu, by0), s1 = mx_scale<FMT>(pr >> 16, by1);
+        sr[0] = __uint_as_float(dpp<0x00>(__float_as_uint(s0)));
+        sr[1] = __uint_as_float(dpp<0x00>(__float_as_uint(s1)));
+        sr[2] = __uint_as_float(dpp<0x55>(__float_as_uint(s0)));
+        sr[3] = __uint_as_float(dpp<0x55>(__float_as_uint(s1)));
+        sr[4] = __uint_as_float(dpp<0xAA>(__float_as_uint(s0)));
+        sr[5] = __uint_as_float(dpp<0xAA>(__float_as_uint(s1)));
+        sr[6] = __uint_as_float(dpp<0xFF>(__float_as_uint(s0)));
+        sr[7] = __uint_as_float(dpp<0xFF>(__float_as_uint(s1)));
+        if (q != nullptr && valid) {
+          uint8_t* o = static_cast<uint8_t*>(sq) + (row + 2 * b) * row_blocks + col / 32;
+          o[0] = (uint8_t)by0;
+          o[row_blocks] = (uint8_t)by1;
+        }
+        // MX columns: lanes of 16-lane row qd compute columns 2qd, 2qd+1
+        const uint32_t pc = pick4(C[0], C[1], C[2], C[3], qd);
+        uint32_t cb0, cb1;
+        const float t0 = mx_scale<FMT>(pc & 0xffffu, cb0), t1 = mx_scale<FMT>(pc >> 16, cb1);
+        rows_gather(t0, t1, sc);
+        // byte w of colb[c] is column c's scale for this wave's 32 rows;
+        // written out after the tile's barrier, one dword per column
+        uint8_t* cb = reinterpret_cast<uint8_t*>(colb[buf]) + (8 * tc + 2 * qd) * 4 + w;
+        cb[0] = (uint8_t)cb0;
+        cb[4] = (uint8_t)cb1;
       }
     }
 
-    // ---- column-wise copy: scale, cast, transpose through LDS, qT stores
     uint32_t* T = tile[buf];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        b[i] = cvt4<FMT>(row_elem(v[i], 4 * k) * sc[4 * k], row_elem(v[i], 4 * k + 1) * sc[4 * k + 1],
-                         row_elem(v[i], 4 * k + 2) * sc[4 * k + 2], row_elem(v[i], 4 * k + 3) * sc[4 * k + 3]);
-      uint32_t col4[4];
-      transpose4x4(b[0], b[1], b[2], b[3], col4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T[qt_word(16 * c + 4 * k + i, a)] = col4[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int col = (t >> 3) + 32 * p, k = t & 7;
-      if (col < cv && 16 * k < rv) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(&T[qt_word(col, 4 * k)]);
-        *reinterpret_cast<uint4*>(qT + (c0 + col) * rows + r0 + 16 * k) = wv;
+    if (valid) {
+      uint8_t* qrow = q != nullptr ? q + row * cols + col : nullptr;
+      if constexpr (KIND == kTBlock128) {
+        if (nan_wave)
+          quant_t_emit_uniform<FMT, true>(v, sr[0], qrow, cols, T, tc, tr);
+        else
+          quant_t_emit_uniform<FMT, false>(v, sr[0], qrow, cols, T, tc, tr);
+      } else {
+        if (nan_wave)
+          quant_t_emit<FMT, true>(v, sr, sc, qrow, cols, T, tc, tr);
+        else
+          quant_t_emit<FMT, false>(v, sr, sc, qrow, cols, T, tc, tr);
       }
     }
-    // column scales of the transposed copy
-    if constexpr (KIND == kTBlock1) {
-      if (t < 8)
+    // qT stores: thread t writes 16 bytes (rows 16k .. 16k+15, k = t % 8) of
+    // qT rows t / 8 + 32p, so 8 lanes write a qT row's 128 bytes.  The tile
+    // is double-buffered: the next tile's writes go to the other half, and
+    // the one after waits for this tile's barrier.
+    __syncthreads();
+    if constexpr (KIND == kTMX) {
+      // column scales: thread c < cv writes column c's bytes for the tile's
+      // rv / 32 row blocks, as one dword when they are whole and aligned
+      if (t < cv) {
+        const uint32_t b4 = colb[buf][t];
+        uint8_t* o = static_cast<uint8_t*>(sqT) + (c0 + t) * col_blocks + r0 / 32;
+        if (rv == 128 && (col_blocks & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(o) = b4;
+        } else {
+          for (int ww = 0; ww < rv / 32; ++ww) o[ww] = (uint8_t)(b4 >> (8 * ww));
+        }
+      }
+    }
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          static_cast<float*>(sqT)[(c0 + 16 * c + j) * col_blocks + r0 / 128] = 1.0f / sc[j];
-    } else if constexpr (KIND == kTMX) {
-      if (lane < 8 && 32 * w < rv && 16 * c < cv)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          static_cast<uint8_t*>(sqT)[(c0 + 16 * c + j) * col_blocks + r0 / 32 + w] = (uint8_t)cbyte[j];
-    } else {
-      if (t == 0) static_cast<float*>(sqT)[(c0 / 128) * col_blocks + r0 / 128] = 1.0f / st;
+    for (int p = 0; p < 4; ++p) {
+      const int c = (t >> 3) + 32 * p, k = t & 7;
+      if (c < cv && 16 * k < rv)
+        *reinterpret_cast<uint4*>(qT + (c0 + c) * rows + r0 + 16 * k) =
+            *reinterpret_cast<const uint4*>(&T[qt8_word(c, 4 * k)]);
     }
   }
 }
