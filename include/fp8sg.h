@@ -23,13 +23,15 @@
  *               the caller.  Tensors are dense and row-major.  The calls that
  *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out,
  *               fp8_quantize_tensor_current,
- *               fp8_gemm_fprop_fused with y_amax) reduce through a 256 KB
- *               buffer of partial maxima that the
- *               library allocates (hipMalloc) on the first such call on each
- *               (device, stream) pair and keeps until the process ends; calls
- *               on one stream run in order and share it, calls on different
- *               streams never do.  If that first allocation fails the call
- *               returns FP8_ERR_HIP.  No other call allocates.
+ *               fp8_gemm_fprop_fused with y_amax) reduce through a 276 KB
+ *               workspace (256 KB of partial maxima, 20 KB of grid-wide
+ *               maximum words) that the library allocates (hipMalloc, and
+ *               clears the maximum words on the stream) on the first such
+ *               call on each (device, stream) pair and keeps until the
+ *               process ends; calls on one stream run in order and share it,
+ *               calls on different streams never do.  That first call must
+ *               not be made under stream capture.  If the allocation fails
+ *               the call returns FP8_ERR_HIP.  No other call allocates.
  *   Stream      `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *               enqueue kernels and return; nothing synchronises.  Outputs are
  *               valid once the stream has passed the call.
@@ -119,9 +121,16 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
 /* Per-tensor current scaling in one call: amax -> scale pair -> cast, the
  * sequence fp8_amax + fp8_quantize_tensor with identical results
  * ([colossal] real-time scaling takes the scale from the current tensor;
- * [guide] three scaling algorithms).  Two launches: the amax pass, then the
- * cast, whose workgroups each reduce the amax pass's partial maxima and
- * derive the scale themselves (no separate finalize).
+ * [guide] three scaling algorithms).  Without qT, when the tensor fits the
+ * registers of a grid the device holds at once (up to about 50M elements on
+ * MI355X), one launch: each thread keeps its share of x in registers, a
+ * grid-wide maximum built from device-scope atomics gives every workgroup
+ * the amax, and the workgroups cast what they hold, so x is read once.
+ * Otherwise two launches: the amax pass, then the cast, whose workgroups
+ * each reduce the amax pass's partial maxima and derive the scale
+ * themselves.  The one-launch grid waits on itself: if other work keeps
+ * part of it from being resident for several milliseconds, the waiting
+ * workgroups reduce all of x themselves (same result, slower).
  *   x_bf16     [rows][cols] BF16, cols % 16 == 0
  *   q          out uint8 [rows][cols];  qT  out [cols][rows], nullable
  *              (rows % 16 == 0)

@@ -228,6 +228,151 @@ __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x
   }
 }
 
+// Current scaling in one launch (BF16 input, no transposed copy), for
+// tensors that fit in the registers of a grid small enough to be resident at
+// once (occupancy times CUs): each thread loads U 16-byte vectors and keeps
+// them; a grid-wide maximum gives every workgroup the tensor's amax, from
+// which it derives the scale and casts the vectors it holds.  The input is
+// read once instead of twice (amax pass, then cast).
+//
+// The grid-wide maximum uses device-coherent atomics only (agent-scope
+// fences would write back and invalidate whole L2s, which costs more than
+// the pass it saves).  Its words live in the per-stream workspace after the
+// partials, zero when allocated, each in a cache line of its own (kLine
+// words).  Workgroups form groups of kGroup:
+//   * a workgroup reads its group's flag (a generation number and a value),
+//     atomically maxes its maximum into the group's word, then (once that
+//     returned) adds 1 to the group's counter;
+//   * the group's last arrival reads the group's word and does the same
+//     with the top word and counter;
+//   * the last of those reads the top word (the amax), resets every counter
+//     and word, and writes (generation + 1, amax) to all group flags;
+//   * the others poll their group's flag with relaxed loads (at most kGroup
+//     pollers per line, so no memory channel is flooded).
+// A returning atomic has been performed when it returns, so each maximum is
+// in place before its arrival is counted.  Same-address atomics serialize,
+// so a flat counter would cost every arrival in turn; here a chain is at
+// most kGroup + kMaxGroups long.
+// The wait is bounded: a grid that is not all resident (other work holding
+// CUs, such as a second such launch on another stream) could otherwise wait
+// for ever.  A workgroup whose wait runs out (kSpinLimit polls, a few ms)
+// reduces the whole input itself, so the result is the same, only slower.
+constexpr int kSpinLimit = 1 << 15;
+constexpr int kLine = 32;                             // words per 128-byte line
+constexpr int kGroup = 32;                            // workgroups per group
+constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
+constexpr uint32_t kNoMax = 0xFFFFFFFFu;              // above any magnitude: the wait ran out
+static_assert((2 * kMaxGroups + 1) * kLine <= kBarrierWords, "barrier words");
+__device__ __forceinline__ uint32_t* gm_cnt(uint32_t* w, int g) { return w + g * kLine; }
+__device__ __forceinline__ uint32_t* gm_max(uint32_t* w, int g) { return w + g * kLine + 1; }
+__device__ __forceinline__ uint64_t* gm_flag(uint32_t* w, int g) {
+  return reinterpret_cast<uint64_t*>(w + (kMaxGroups + g) * kLine);
+}
+__device__ __forceinline__ uint32_t* gm_top_cnt(uint32_t* w) { return w + 2 * kMaxGroups * kLine; }
+__device__ __forceinline__ uint32_t* gm_top_max(uint32_t* w) {
+  return w + 2 * kMaxGroups * kLine + 1;
+}
+// 0, computed from v in a way the compiler cannot see through: an atomic
+// that takes it waits for v, i.e. for the atomic that produced v.
+__device__ __forceinline__ uint32_t after(uint32_t v) {
+  uint32_t z;
+  asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
+  return z;
+}
+__device__ __forceinline__ uint32_t atomic_max_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The largest m over the grid's workgroups, in every workgroup (kNoMax if
+// the wait ran out).  All threads call it; thread 0 does the work.
+__device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t nblocks,
+                                             uint32_t* sh) {
+  if (threadIdx.x == 0) {
+    const int g = (int)(blockIdx.x / kGroup);
+    const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
+    const uint32_t gsize = min((uint32_t)kGroup, nblocks - (uint32_t)g * kGroup);
+    const uint64_t f0 = __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t gen = (uint32_t)(f0 >> 32);
+    const uint32_t mo = atomic_max_agent(gm_max(w, g), m + after((uint32_t)f0));
+    const uint32_t arrived = atomic_add_agent(gm_cnt(w, g), 1u + after(mo));
+    uint32_t res = kNoMax;
+    bool last = false;
+    if (arrived + 1 == gsize) {
+      const uint32_t gmx = atomic_max_agent(gm_max(w, g), after(arrived));
+      const uint32_t to = atomic_max_agent(gm_top_max(w), gmx);
+      last = atomic_add_agent(gm_top_cnt(w), 1u + after(to)) + 1 == ngroups;
+    }
+    if (last) {
+      res = atomic_max_agent(gm_top_max(w), 0u);
+      const uint32_t z = after(res);
+      for (uint32_t i = 0; i < ngroups; ++i) {
+        __hip_atomic_store(gm_cnt(w, (int)i), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gm_max(w, (int)i), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(gm_top_cnt(w), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gm_top_max(w), z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t f1 = ((uint64_t)(gen + 1u) << 32) | res;
+      for (int i = 0; i < kMaxGroups; ++i)
+        __hip_atomic_store(gm_flag(w, i), f1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      for (int spin = 0; spin < kSpinLimit; ++spin) {
+        const uint64_t f =
+            __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(f >> 32) != gen) {
+          res = (uint32_t)f;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    *sh = res;
+  }
+  __syncthreads();
+  return *sh;
+}
+
+template <int FMT, int U>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
+    const uint4* __restrict__ x, int64_t nvec, uint2* __restrict__ q, uint32_t* __restrict__ gw,
+    float* __restrict__ amax, float* __restrict__ scale, float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t sh;
+  // workgroup-uniform bases, 32-bit per-lane offsets
+  const int64_t wg0 = (int64_t)blockIdx.x * (U * kThreads);
+  const uint4* xw = x + wg0;
+  uint2* qw = q + wg0;
+  const int nv = (int)min<int64_t>(nvec - wg0, (int64_t)U * kThreads);   // this workgroup's vectors
+  const int t = threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    v[u] = t + u * kThreads < nv ? ld_stream(&xw[t + u * kThreads]) : make_uint4(0, 0, 0, 0);
+  uint32_t m = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
+  m = block_max_u32<kThreads>(m << 16, red);
+  uint32_t a = grid_max(gw, m, gridDim.x, &sh);
+  if (a == kNoMax) {
+    a = 0;
+    for (int64_t i = t; i < nvec; i += kThreads) a = max(a, absmax8(x[i]) << 16);
+    a = block_max_u32<kThreads>(a, red);
+  }
+  const float am = __uint_as_float(a);
+  const float s = scale_from_amax<FMT>(am);
+  if (blockIdx.x == 0 && t == 0) {
+    *amax = am;
+    if (scale) *scale = s;
+    *scale_inv = 1.0f / s;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (t + u * kThreads < nv) qw[t + u * kThreads] = cast8<FMT>(v[u], s);
+}
+
 // 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
 // into columns: out[i] = bytes (a_i, b_i, c_i, d_i).
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
@@ -834,8 +979,10 @@ int grid_for(int64_t work_items, int per_block) {
 }  // namespace
 
 // One partial-maximum buffer (kWorkspaceWords words: a quantise launch uses
-// at most kMaxPartials, a GEMM with a fused amax one per output tile) per
-// (device, stream), allocated on first use and kept until the process ends.
+// at most kMaxPartials, a GEMM with a fused amax one per output tile), then
+// kBarrierWords for the one-launch current scaling's grid barrier, per
+// (device, stream), allocated (and the barrier words cleared) on first use
+// and kept until the process ends.
 // Work on one stream runs in order, so successive calls on a stream share its
 // buffer safely; calls on different streams never share one.
 struct StreamBuffer {
@@ -857,8 +1004,15 @@ hipError_t stream_partials(hipStream_t s, uint32_t** out) {
       return hipSuccess;
     }
   void* p = nullptr;
-  err = hipMalloc(&p, kWorkspaceWords * sizeof(uint32_t));
+  err = hipMalloc(&p, (kWorkspaceWords + kBarrierWords) * sizeof(uint32_t));
   if (err != hipSuccess) return err;
+  // the grid-barrier words start at zero
+  err = hipMemsetAsync(static_cast<uint32_t*>(p) + kWorkspaceWords, 0,
+                       kBarrierWords * sizeof(uint32_t), s);
+  if (err != hipSuccess) {
+    (void)hipFree(p);
+    return err;
+  }
   g_partials.push_back({dev, s, static_cast<uint32_t*>(p)});
   *out = static_cast<uint32_t*>(p);
   return hipSuccess;
@@ -968,6 +1122,45 @@ hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int
 
 // Current scaling: the amax launch writes partials, the cast reduces them
 // itself (no separate finalize launch).
+// Largest grid of k_amax_cast<FMT, U> the current device holds at once
+// (0 if unknown), cached per device.
+template <int FMT, int U>
+static int coop_capacity() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_amax_cast<FMT, U>, kThreads, 0) !=
+        hipSuccess)
+      per_cu = 0;
+    cached[dev] = per_cu > 0 ? per_cu * device_cu_count() : -1;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+// One launch of k_amax_cast<FMT, U> if nvec vectors fit a grid the device
+// holds at once (and the partial buffer); *done tells whether it ran.
+// (A cooperative launch would guarantee residency but costs this runtime
+// far more than the pass it saves; the grid maximum's bounded wait covers
+// the rare grid that is not all resident.)
+template <int FMT, int U>
+static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_t* part,
+                                float* amax, float* scale, float* scale_inv, hipStream_t s,
+                                bool* done) {
+  const int64_t g = (nvec + (int64_t)U * kThreads - 1) / ((int64_t)U * kThreads);
+  const int cap = coop_capacity<FMT, U>();
+  if (g > cap || g > kMaxPartials) return hipSuccess;
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  uint32_t* gw = part + kWorkspaceWords;
+  hipLaunchKernelGGL((k_amax_cast<FMT, U>), dim3((unsigned)g), dim3(kThreads), 0, s, xv, nvec,
+                     qv, gw, amax, scale, scale_inv);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) *done = true;
+  return err;
+}
+
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
                                    float* scale_inv, hipStream_t s, int in) {
@@ -976,6 +1169,20 @@ hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, in
   uint32_t* part = nullptr;
   hipError_t err = stream_partials(s, &part);
   if (err != hipSuccess) return err;
+  // One launch when the tensor fits the registers of a co-resident grid:
+  // BF16, whole 16-byte vectors, no transposed copy.
+  if (in == kInBF16 && qT == nullptr && n % 8 == 0) {
+    bool done = false;
+    FP8SG_FMT_DISPATCH(fmt, {
+      err = try_amax_cast<F, 8>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+      if (err == hipSuccess && !done)
+        err = try_amax_cast<F, 16>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+      if (err == hipSuccess && !done)
+        err = try_amax_cast<F, 24>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+    });
+    if (err != hipSuccess) return err;
+    if (done) return hipSuccess;
+  }
   const int per = in == kInBF16 ? 8 : 4;
   const int64_t nvec = n / per;
   const int ntail = (int)(n - nvec * per);

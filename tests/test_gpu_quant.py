@@ -155,11 +155,16 @@ def test_quantize_mx(F, orc, shape, fmt):
 
 @pytest.mark.parametrize("shape,transposed", [((0, 16), False), ((1, 16), False),
                                               ((37, 48), False), ((272, 384), True),
-                                              ((4112, 8208), False), ((4112, 8208), True)])
+                                              ((3072, 8192), False), ((4112, 8208), False),
+                                              ((4112, 8208), True), ((6400, 8192), False)])
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 def test_quantize_tensor_current(F, orc, shape, transposed, fmt):
     """One-call current scaling = fp8_amax + fp8_quantize_tensor, bit for bit,
-    and the oracle's amax / scale rule / cast."""
+    and the oracle's amax / scale rule / cast.  The shapes cover the one-launch
+    path at each register budget (128, 256 and 384 bytes per thread: 1x16,
+    37x48 and 3072x8192; 4112x8208; the 11008x4096 weight in the workload
+    tests) and the two-launch fallbacks (transposed copy; 6400x8192, more than
+    the registers of a co-resident grid hold)."""
     x = rand_bits(shape, 101 + shape[1], 2.0, specials=True)
     xd = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device=DEV)
     R, C = shape
