@@ -155,7 +155,7 @@ void k_gemm8(Args p) {
     const int sc = (kt >> 2) & 1, sw = kt & 3;
     float sa_f[NF];
     float sb_u = 0.f;
-    int ea[NF];
+    int ea[NF], eb[2];
     if constexpr (MODE == kBlock) {
       const float* S = reinterpret_cast<const float*>(lS[sc]);
 #pragma unroll
@@ -169,6 +169,7 @@ void k_gemm8(Args p) {
       const uint8_t* S = reinterpret_cast<const uint8_t*>(lS[sc]);
 #pragma unroll
       for (int f = 0; f < NF; ++f) ea[f] = S[((wm * WM + f * 16 + lr) * 4 + sw) * 4 + g];
+      eb[0] = S[((256 + wn * WN + lr) * 4 + sw) * 4 + g];
     }
     if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -177,15 +178,19 @@ void k_gemm8(Args p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j + 1 < NJ) bf[(j + 1) & 1] = load_frag(Bs, wn * WN + (j + 1) * 16);
+      if constexpr (MODE == kMX) {
+        // the next column's B scale byte, one column ahead like its fragment
+        if (j + 1 < NJ)
+          eb[(j + 1) & 1] = reinterpret_cast<const uint8_t*>(
+              lS[sc])[((256 + wn * WN + (j + 1) * 16 + lr) * 4 + sw) * 4 + g];
+      }
       if constexpr (MODE == kTensor) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[f][j] = mfma<FB, FA>(bf[j & 1], af[f], acc[f][j]);
       } else if constexpr (MODE == kMX) {
-        const uint8_t* S = reinterpret_cast<const uint8_t*>(lS[sc]);
-        const int eb = S[((256 + wn * WN + j * 16 + lr) * 4 + sw) * 4 + g];
 #pragma unroll
         for (int f = 0; f < NF; ++f)
-          acc[f][j] = mfma_mx<FB, FA>(bf[j & 1], af[f], acc[f][j], eb, ea[f]);
+          acc[f][j] = mfma_mx<FB, FA>(bf[j & 1], af[f], acc[f][j], eb[j & 1], ea[f]);
       } else {
 #pragma unroll
         for (int f = 0; f < NF; ++f)
