@@ -184,6 +184,32 @@ def test_quantize_tensor_current(F, orc, shape, transposed, fmt):
         assert np.array_equal(bytes8(qT), wqT)
 
 
+def test_quantize_tensor_current_concurrent_streams(F, orc):
+    """Two one-launch current-scaling calls running at once on different
+    streams, each grid as large as the device holds.  However the two grids'
+    workgroups interleave (one grid can keep the other from being resident),
+    both results are the oracle's, bit for bit: a workgroup whose grid-wide
+    wait runs out reduces the whole input itself."""
+    shape = (4096, 8192)
+    xs = [rand_bits(shape, 700 + i, 3.0) for i in range(2)]
+    dx = [dev_bf16(x) for x in xs]
+    streams = [torch.cuda.Stream() for _ in xs]
+    outs = [(empty_dev(shape, torch.uint8),) + tuple(empty_dev(1, torch.float32) for _ in range(3))
+            for _ in xs]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for x, st, (q, am, s, si) in zip(dx, streams, outs):
+            F.fp8_quantize_tensor_current(x, E4M3, q, None, am, s, si, stream=st)
+    torch.cuda.synchronize()
+    for x, (q, am, s, si) in zip(xs, outs):
+        wa = orc.amax(x)
+        ws, wsi = orc.scale_from_amax(wa, E4M3)
+        assert f32(am)[0].view(np.uint32) == np.float32(wa).view(np.uint32)
+        assert f32(s)[0] == ws and f32(si)[0] == wsi
+        wq, _, _ = orc.quantize_tensor(x, E4M3, ws)
+        assert np.array_equal(bytes8(q), wq)
+
+
 def rand_f32(shape, seed, scale=1.0):
     """FP32 values with a wide magnitude range and a few specials."""
     rng = np.random.Generator(np.random.PCG64(seed))
