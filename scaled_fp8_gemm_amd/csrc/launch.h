@@ -12,8 +12,10 @@ int device_cu_count();
 // Per-(device, stream) buffer of kWorkspaceWords partial maxima (FP32
 // magnitude bits), allocated on first use.
 constexpr int kWorkspaceWords = 1 << 16;
-// followed by kBarrierWords words for a grid barrier (zero when allocated)
-constexpr int kBarrierWords = 160 * 32;
+// followed by kGridMaxWords words for the grid-wide maximum of the one-launch
+// current scaling (counters, maxima and flags, one 128-byte line each; zero
+// when allocated)
+constexpr int kGridMaxWords = 160 * 32;
 hipError_t stream_partials(hipStream_t s, uint32_t** out);
 // amax[0] = the largest of part[0 .. n-1], as an FP32 value.
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s);

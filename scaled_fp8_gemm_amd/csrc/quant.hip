@@ -262,7 +262,7 @@ constexpr int kLine = 32;                             // words per 128-byte line
 constexpr int kGroup = 32;                            // workgroups per group
 constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
 constexpr uint32_t kNoMax = 0xFFFFFFFFu;              // above any magnitude: the wait ran out
-static_assert((2 * kMaxGroups + 1) * kLine <= kBarrierWords, "barrier words");
+static_assert((2 * kMaxGroups + 1) * kLine <= kGridMaxWords, "grid-wide maximum words");
 __device__ __forceinline__ uint32_t* gm_cnt(uint32_t* w, int g) { return w + g * kLine; }
 __device__ __forceinline__ uint32_t* gm_max(uint32_t* w, int g) { return w + g * kLine + 1; }
 __device__ __forceinline__ uint64_t* gm_flag(uint32_t* w, int g) {
@@ -980,8 +980,8 @@ int grid_for(int64_t work_items, int per_block) {
 
 // One partial-maximum buffer (kWorkspaceWords words: a quantise launch uses
 // at most kMaxPartials, a GEMM with a fused amax one per output tile), then
-// kBarrierWords for the one-launch current scaling's grid barrier, per
-// (device, stream), allocated (and the barrier words cleared) on first use
+// kGridMaxWords for the one-launch current scaling's grid-wide maximum, per
+// (device, stream), allocated (and those words cleared) on first use
 // and kept until the process ends.
 // Work on one stream runs in order, so successive calls on a stream share its
 // buffer safely; calls on different streams never share one.
@@ -1004,11 +1004,11 @@ hipError_t stream_partials(hipStream_t s, uint32_t** out) {
       return hipSuccess;
     }
   void* p = nullptr;
-  err = hipMalloc(&p, (kWorkspaceWords + kBarrierWords) * sizeof(uint32_t));
+  err = hipMalloc(&p, (kWorkspaceWords + kGridMaxWords) * sizeof(uint32_t));
   if (err != hipSuccess) return err;
-  // the grid-barrier words start at zero
+  // the grid-wide maximum's words start at zero
   err = hipMemsetAsync(static_cast<uint32_t*>(p) + kWorkspaceWords, 0,
-                       kBarrierWords * sizeof(uint32_t), s);
+                       kGridMaxWords * sizeof(uint32_t), s);
   if (err != hipSuccess) {
     (void)hipFree(p);
     return err;
