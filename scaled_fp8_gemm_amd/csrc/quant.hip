@@ -1174,9 +1174,9 @@ hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, in
   if (in == kInBF16 && qT == nullptr && n % 8 == 0) {
     bool done = false;
     FP8SG_FMT_DISPATCH(fmt, {
-      err = try_amax_cast<F, 8>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
-      if (err == hipSuccess && !done)
-        err = try_amax_cast<F, 16>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+      // 16 vectors per thread (fewer workgroups, a shorter arrival chain) up
+      // to ~42M elements, 24 up to ~50M
+      err = try_amax_cast<F, 16>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
       if (err == hipSuccess && !done)
         err = try_amax_cast<F, 24>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
     });

@@ -161,8 +161,8 @@ def test_quantize_mx(F, orc, shape, fmt):
 def test_quantize_tensor_current(F, orc, shape, transposed, fmt):
     """One-call current scaling = fp8_amax + fp8_quantize_tensor, bit for bit,
     and the oracle's amax / scale rule / cast.  The shapes cover the one-launch
-    path at each register budget (128, 256 and 384 bytes per thread: 1x16,
-    37x48 and 3072x8192; 4112x8208; the 11008x4096 weight in the workload
+    path at both register budgets (256 bytes per thread: 1x16, 37x48,
+    3072x8192 and 4112x8208; 384 bytes: the 11008x4096 weight in the workload
     tests) and the two-launch fallbacks (transposed copy; 6400x8192, more than
     the registers of a co-resident grid hold)."""
     x = rand_bits(shape, 101 + shape[1], 2.0, specials=True)
