@@ -341,16 +341,24 @@ __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
     float* __restrict__ amax, float* __restrict__ scale, float* __restrict__ scale_inv) {
   __shared__ uint32_t red[kThreads / 64];
   __shared__ uint32_t sh;
-  // workgroup-uniform bases, 32-bit per-lane offsets
+  // This workgroup's vectors through buffer descriptors covering exactly
+  // them: one 32-bit lane offset in a VGPR, the vector's offset in an SGPR,
+  // and the range check instead of predication (loads past the end read 0,
+  // stores past it are dropped).
   const int64_t wg0 = (int64_t)blockIdx.x * (U * kThreads);
-  const uint4* xw = x + wg0;
-  uint2* qw = q + wg0;
   const int nv = (int)min<int64_t>(nvec - wg0, (int64_t)U * kThreads);   // this workgroup's vectors
   const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(x + wg0), (short)0, nv * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(q + wg0), (short)0, nv * 8, 0x00020000);
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   uint4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    v[u] = t + u * kThreads < nv ? ld_stream(&xw[t + u * kThreads]) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < U; ++u) {
+    const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 16, u * kThreads * 16, 0);
+    v[u] = make_uint4(r[0], r[1], r[2], r[3]);
+  }
   uint32_t m = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
@@ -369,8 +377,13 @@ __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
     *scale_inv = 1.0f / s;
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (t + u * kThreads < nv) qw[t + u * kThreads] = cast8<FMT>(v[u], s);
+  for (int u = 0; u < U; ++u) {
+    const uint2 c = cast8<FMT>(v[u], s);
+    u32x2_t w;
+    w[0] = c.x;
+    w[1] = c.y;
+    __builtin_amdgcn_raw_buffer_store_b64(w, qr, t * 8, u * kThreads * 8, 0);
+  }
 }
 
 // 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
@@ -1174,8 +1187,8 @@ hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, in
   if (in == kInBF16 && qT == nullptr && n % 8 == 0) {
     bool done = false;
     FP8SG_FMT_DISPATCH(fmt, {
-      // 16 vectors per thread (fewer workgroups, a shorter arrival chain) up
-      // to ~42M elements, 24 up to ~50M
+      // 16 vectors per thread (fewer workgroups, a shorter arrival chain; on
+      // MI355X up to ~50M elements), then 24
       err = try_amax_cast<F, 16>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
       if (err == hipSuccess && !done)
         err = try_amax_cast<F, 24>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
