@@ -280,10 +280,10 @@ class Path:
 
 
 def cpu_baseline(key):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    amax, scale and cast of the whole X and W (C oracle, OpenMP), and the
-    GEMM for a sample of output rows (numpy FP64 matmul of the decoded
-    operands); the step time is extrapolated to all rows."""
+    """The oracle as it stands, on whole steps of the same workload: amax,
+    scale and cast of all of X and W (C oracle, OpenMP), then the full GEMM
+    (numpy FP64 matmul of the decoded operands), repeated until about 10 s of
+    CPU work (at least one step, at most 8)."""
     import numpy as np
     import torch
     from oracle import oracle as orc
@@ -293,24 +293,32 @@ def cpu_baseline(key):
     x = gen.make_x(cfg, "cpu").view(torch.int16).numpy().view(np.uint16)
     w = gen.make_w(cfg, "cpu").view(torch.int16).numpy().view(np.uint16)
     orc.lib()
-    rows = 256
-    t0 = time.perf_counter()
-    sx, six = orc.scale_from_amax(orc.amax(x), orc.E4M3)
-    sw, siw = orc.scale_from_amax(orc.amax(w), orc.E4M3)
-    xq, _, _ = orc.quantize_tensor(x, orc.E4M3, sx)
-    wq, _, _ = orc.quantize_tensor(w, orc.E4M3, sw)
-    t1 = time.perf_counter()
-    orc.gemm_full(xq[:rows], wq, orc.E4M3, orc.E4M3, orc.SCALE_TENSOR,
-                  np.float32([six]), np.float32([siw]))
-    t2 = time.perf_counter()
-    t_step = (t1 - t0) + (t2 - t1) * (M / rows)
+    t_quant = t_gemm = 0.0
+    steps = 0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        sx, six = orc.scale_from_amax(orc.amax(x), orc.E4M3)
+        sw, siw = orc.scale_from_amax(orc.amax(w), orc.E4M3)
+        xq, _, _ = orc.quantize_tensor(x, orc.E4M3, sx)
+        wq, _, _ = orc.quantize_tensor(w, orc.E4M3, sw)
+        t1 = time.perf_counter()
+        orc.gemm_full(xq, wq, orc.E4M3, orc.E4M3, orc.SCALE_TENSOR,
+                      np.float32([six]), np.float32([siw]))
+        t2 = time.perf_counter()
+        t_quant += t1 - t0
+        t_gemm += t2 - t1
+        steps += 1
+        if t2 - t_start >= 10.0 or steps >= 8:
+            break
+    t_step = (t_quant + t_gemm) / steps
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(2.0 * M * N * K / t_step / 1e12, 6), "unit": "TFLOP/s",
             "cores": cores, "kind": "oracle",
-            "sample": (f"amax+scale+E4M3 cast of all of X[{M}x{K}] and W[{N}x{K}] "
-                       f"({t1 - t0:.2f} s) + FP64 GEMM of {rows} of {M} output rows "
-                       f"({t2 - t1:.2f} s), extrapolated to the full step "
-                       f"({t_step:.1f} s)")}
+            "sample": (f"{steps} whole step(s): amax+scale+E4M3 cast of all of X[{M}x{K}] and "
+                       f"W[{N}x{K}] ({t_quant / steps:.2f} s per step) + FP64 GEMM of all "
+                       f"{M}x{N} outputs ({t_gemm / steps:.2f} s per step); "
+                       f"{t_quant + t_gemm:.1f} s in total")}
 
 
 def main():
