@@ -324,8 +324,8 @@ def cpu_baseline(key):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(the multi-GPU sharding is described, not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
+                                   "(how the path would shard is described, not implemented)"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
