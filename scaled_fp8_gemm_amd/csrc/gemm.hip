@@ -24,8 +24,9 @@
 //   * the two waves of a SIMD hide each other's LDS and barrier latency in
 //     every mode.
 // Per-step scales (FP32 block scales, or the four E8M0 bytes of a row's
-// 128-K step) travel by LDS DMA with the tiles: one 4-byte load per tile row
-// and operand, 64 rows per wave.
+// 128-K step) travel by LDS DMA with the tiles, four steps at a time: one
+// 16-byte load per tile row and operand every fourth step, 64 rows per wave,
+// into a double-buffered chunk.
 #include "gemm_common.h"
 #include "launch.h"
 
