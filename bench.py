@@ -283,7 +283,7 @@ def cpu_baseline(key):
     """The oracle as it stands, on whole steps of the same workload: amax,
     scale and cast of all of X and W (C oracle, OpenMP), then the full GEMM
     (numpy FP64 matmul of the decoded operands), repeated until about 10 s of
-    CPU work (at least one step, at most 8)."""
+    CPU work (at least one step, at most 20)."""
     import numpy as np
     import torch
     from oracle import oracle as orc
@@ -309,7 +309,7 @@ def cpu_baseline(key):
         t_quant += t1 - t0
         t_gemm += t2 - t1
         steps += 1
-        if t2 - t_start >= 10.0 or steps >= 8:
+        if t2 - t_start >= 10.0 or steps >= 20:
             break
     t_step = (t_quant + t_gemm) / steps
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
