@@ -222,8 +222,8 @@ def test_layer_three_gemms_mx(F, orc, M, K, N):
 @pytest.mark.parametrize("M,N,K", [(256, 384, 512), (384, 72, 90)])
 def test_wgrad_f32_store_and_accumulate(F, orc, scaling, M, N, K):
     """FP32 wgrad: stored, then accumulated onto a previous FP32 gradient."""
-    if scaling == "block" and (M % 128 or K % 128 or N % 128):
-        pytest.skip("blockwise needs 128-multiples")
+    if scaling == "block" and M % 128:
+        pytest.skip("1x128 blocks need a contraction that is a multiple of 128")
     if scaling == "mx_k32":
         M = 352                                   # MX contraction % 128 != 0
     fa, fb = (E5M2, E4M3) if scaling == "tensor" else (E4M3, E4M3)
