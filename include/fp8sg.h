@@ -22,9 +22,9 @@
  *   Memory      Every pointer argument except `stream` is device memory owned by
  *               the caller.  Tensors are dense and row-major.  The calls that
  *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out,
- *               fp8_quantize_tensor_current,
- *               fp8_gemm_fprop_fused with y_amax) reduce through a 276 KB
- *               workspace (256 KB of partial maxima, 20 KB of grid-wide
+ *               fp8_quantize_tensor_current, fp8_quantize_pair_current,
+ *               fp8_gemm_fprop_fused with y_amax) reduce through a 289 KB
+ *               workspace (256 KB of partial maxima, 33 KB of grid-wide
  *               maximum words) that the library allocates (hipMalloc, and
  *               clears the maximum words on the stream) on the first such
  *               call on each (device, stream) pair and keeps until the
@@ -141,6 +141,31 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
 fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64_t cols,
                                          int32_t fmt, uint8_t* q, uint8_t* qT, float* amax,
                                          float* scale, float* scale_inv, void* stream);
+
+/* Per-tensor current scaling of a GEMM's two operands (for instance X and W
+ * of fprop) in one call: the results are exactly those of
+ * fp8_quantize_tensor_current on each tensor without a transposed copy
+ * ([colossal] real-time scaling; [guide] three scaling algorithms: each
+ * tensor's scale comes from its own current maximum).  When the device holds
+ * both tensors at once (about 67M elements in total on MI355X), one launch
+ * does both: each workgroup keeps its share of one tensor in VGPRs and LDS,
+ * and each tensor has a grid-wide maximum of its own, so the two tensors'
+ * reads, waits and casts overlap.  Otherwise one fp8_quantize_tensor_current
+ * per tensor.  The one-launch wait is bounded as in that call.
+ *   a_bf16, b_bf16   [rows][cols] BF16 each, cols % 16 == 0
+ *   a_fmt, b_fmt     their FP8 formats
+ *   a_q, b_q         out uint8 [rows][cols] each
+ *   a_amax, a_scale, a_scale_inv, b_amax, ...   out float[1] each; the scale
+ *                    pointers are nullable
+ * The two tensors' outputs must not overlap each other or either input.
+ * Uses the workspace described under Memory.  Errors as
+ * fp8_quantize_tensor_current, checked for a, then for b, before any launch. */
+fp8_status_t fp8_quantize_pair_current(const void* a_bf16, int64_t a_rows, int64_t a_cols,
+                                       int32_t a_fmt, uint8_t* a_q, float* a_amax,
+                                       float* a_scale, float* a_scale_inv, const void* b_bf16,
+                                       int64_t b_rows, int64_t b_cols, int32_t b_fmt,
+                                       uint8_t* b_q, float* b_amax, float* b_scale,
+                                       float* b_scale_inv, void* stream);
 
 /* FP32 master-weight input.  [snippets] forward-pass snippet: the master
  * weights are FP32 and are quantised to FP8 for the GEMM.  The same calls as

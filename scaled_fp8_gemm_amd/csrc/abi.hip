@@ -172,6 +172,35 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
                                             scale_inv, st(stream), 0));
 }
 
+static fp8_status_t current_ok(const void* x, int64_t rows, int64_t cols, int32_t fmt,
+                               const uint8_t* q, const float* amax, const float* scale,
+                               const float* scale_inv) {
+  if (!amax || !scale_inv) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x, rows * cols) || !have(q, rows * cols)) return FP8_ERR_NULL;
+  if (cols % 16) return FP8_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(amax, 4) || !aligned(scale_inv, 4) ||
+      (scale && !aligned(scale, 4)))
+    return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+fp8_status_t fp8_quantize_pair_current(const void* a_bf16, int64_t a_rows, int64_t a_cols,
+                                       int32_t a_fmt, uint8_t* a_q, float* a_amax,
+                                       float* a_scale, float* a_scale_inv, const void* b_bf16,
+                                       int64_t b_rows, int64_t b_cols, int32_t b_fmt,
+                                       uint8_t* b_q, float* b_amax, float* b_scale,
+                                       float* b_scale_inv, void* stream) {
+  fp8_status_t e = current_ok(a_bf16, a_rows, a_cols, a_fmt, a_q, a_amax, a_scale, a_scale_inv);
+  if (e != FP8_OK) return e;
+  e = current_ok(b_bf16, b_rows, b_cols, b_fmt, b_q, b_amax, b_scale, b_scale_inv);
+  if (e != FP8_OK) return e;
+  const fp8sg::CurrentTensor ta{a_bf16, a_rows, a_cols, a_fmt, a_q, a_amax, a_scale, a_scale_inv};
+  const fp8sg::CurrentTensor tb{b_bf16, b_rows, b_cols, b_fmt, b_q, b_amax, b_scale, b_scale_inv};
+  return hip(fp8sg::launch_quantize_pair_current(ta, tb, st(stream)));
+}
+
 fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
                                      const float* scale, uint8_t* q, uint8_t* qT,
                                      float* amax_out, void* stream) {

@@ -140,4 +140,65 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return lo | (hi << 16);
 }
 
+// Buffer descriptors and LDS DMA (buffer_load ... lds).
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a __shared__ pointer (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+// Buffer descriptor over `records` bytes from `base` (raw buffer, no stride,
+// range-checked: loads past `records` return zeros).
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t records) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) & 0xffff;
+  r[2] = (int)__builtin_amdgcn_readfirstlane(records);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voffset into LDS
+// at m0 + 16 * lane.  Issued through inline assembly so that the compiler
+// neither models it as an LDS write (which would make it wait for the load
+// before unrelated LDS reads of the other buffer) nor reorders it; completion
+// is awaited explicitly with vmcnt before the workgroup barrier.  m0 is
+// reserved by the compiler, so the sequence restores it.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voffset) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
+
+// The same with 4 bytes per lane (LDS at m0 + 4 * lane).
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voffset) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 }  // namespace fp8sg

@@ -12,10 +12,10 @@ int device_cu_count();
 // Per-(device, stream) buffer of kWorkspaceWords partial maxima (FP32
 // magnitude bits), allocated on first use.
 constexpr int kWorkspaceWords = 1 << 16;
-// followed by kGridMaxWords words for the grid-wide maximum of the one-launch
-// current scaling (counters, maxima and flags, one 128-byte line each; zero
-// when allocated)
-constexpr int kGridMaxWords = 160 * 32;
+// followed by kGridMaxWords words for the grid-wide maxima of the one-launch
+// current scaling (two sets, one per tensor of the paired launch; counters,
+// maxima and flags, one 128-byte line each; zero when allocated)
+constexpr int kGridMaxWords = 260 * 32;
 hipError_t stream_partials(hipStream_t s, uint32_t** out);
 // amax[0] = the largest of part[0 .. n-1], as an FP32 value.
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s);
@@ -26,10 +26,25 @@ hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* sc
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
                                   hipStream_t s, int in);
-// amax -> scale pair -> cast in two launches (current scaling).
+// amax -> scale pair -> cast (current scaling): one launch when the tensor fits
+// a grid the device holds at once, else two.
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
                                    float* scale_inv, hipStream_t s, int in);
+// One BF16 tensor under current scaling, without a transposed copy.
+struct CurrentTensor {
+  const void* x;
+  int64_t rows, cols;
+  int fmt;
+  uint8_t* q;
+  float* amax;
+  float* scale;
+  float* scale_inv;
+};
+// Current scaling of two tensors in one launch when the device holds both
+// at once, else one launch_quantize_current each.
+hipError_t launch_quantize_pair_current(const CurrentTensor& a, const CurrentTensor& b,
+                                        hipStream_t s);
 hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
                                  float* scale, float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,

@@ -262,7 +262,9 @@ constexpr int kLine = 32;                             // words per 128-byte line
 constexpr int kGroup = 32;                            // workgroups per group
 constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
 constexpr uint32_t kNoMax = 0xFFFFFFFFu;              // above any magnitude: the wait ran out
-static_assert((2 * kMaxGroups + 1) * kLine <= kGridMaxWords, "grid-wide maximum words");
+// words of one grid-wide maximum; the paired launch uses two such sets
+constexpr int kGridSetWords = (2 * kMaxGroups + 1) * kLine;
+static_assert(2 * kGridSetWords <= kGridMaxWords, "grid-wide maximum words");
 __device__ __forceinline__ uint32_t* gm_cnt(uint32_t* w, int g) { return w + g * kLine; }
 __device__ __forceinline__ uint32_t* gm_max(uint32_t* w, int g) { return w + g * kLine + 1; }
 __device__ __forceinline__ uint64_t* gm_flag(uint32_t* w, int g) {
@@ -286,12 +288,13 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The largest m over the grid's workgroups, in every workgroup (kNoMax if
-// the wait ran out).  All threads call it; thread 0 does the work.
-__device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t nblocks,
-                                             uint32_t* sh) {
+// The largest m over the nblocks workgroups that share the words at w, in
+// every one of them (kNoMax if the wait ran out); `block` is the calling
+// workgroup's index among them.  All threads call it; thread 0 does the work.
+__device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t block,
+                                             uint32_t nblocks, uint32_t* sh) {
   if (threadIdx.x == 0) {
-    const int g = (int)(blockIdx.x / kGroup);
+    const int g = (int)(block / kGroup);
     const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
     const uint32_t gsize = min((uint32_t)kGroup, nblocks - (uint32_t)g * kGroup);
     const uint64_t f0 = __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -363,7 +366,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
 #pragma unroll
   for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
   m = block_max_u32<kThreads>(m << 16, red);
-  uint32_t a = grid_max(gw, m, gridDim.x, &sh);
+  uint32_t a = grid_max(gw, m, blockIdx.x, gridDim.x, &sh);
   if (a == kNoMax) {
     a = 0;
     for (int64_t i = t; i < nvec; i += kThreads) a = max(a, absmax8(x[i]) << 16);
@@ -384,6 +387,103 @@ __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
     w[1] = c.y;
     __builtin_amdgcn_raw_buffer_store_b64(w, qr, t * 8, u * kThreads * 8, 0);
   }
+}
+
+// One tensor of the paired current-scaling launch.
+struct PairTensor {
+  const uint4* x;       // BF16 input, 16-byte vectors
+  int64_t nvec;
+  uint2* q;             // FP8 output, 8 bytes per vector
+  uint32_t* gw;         // its grid-wide maximum words
+  float* amax;
+  float* scale;
+  float* scale_inv;
+  uint32_t nblocks;     // its workgroups
+};
+struct PairArgs {
+  PairTensor t[2];
+};
+
+// Per-tensor current scaling of one tensor of a pair: as k_amax_cast, with
+// each thread holding U vectors in VGPRs and L more in LDS.  The LDS share is
+// moved there by LDS DMA (buffer_load ... lds), so it never occupies VGPRs:
+// with U = 24, L = 8 four workgroups fit a CU (VGPRs and 128 KB of LDS), so
+// 256 CUs hold 67M BF16 values at once (a LLaMA2-7B up-projection's X and W
+// together), against 50M with registers alone.  Vector u of thread t is the
+// workgroup's vector
+// u * kThreads + t, so every load and store instruction covers 4 KB of
+// contiguous memory per workgroup.
+template <int FMT, int U, int L>
+__device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
+                                               uint4 (*lv)[kThreads], uint32_t* red,
+                                               uint32_t* sh) {
+  constexpr int V = U + L;
+  const int64_t wg0 = (int64_t)b * (V * kThreads);
+  const int nv = (int)min<int64_t>(T.nvec - wg0, (int64_t)V * kThreads);
+  const int t = threadIdx.x;
+  // LDS share first (vectors U .. V-1): lane i of a wave lands at m0 + 16 i,
+  // i.e. at lv[l][t]; reads past the range give zeros
+  const v4i xr4 = make_rsrc(T.x + wg0, (uint32_t)nv * 16u);
+  const uint32_t l0 = lds_addr(&lv[0][t & ~63]);
+#pragma unroll
+  for (int l = 0; l < L; ++l)
+    dma16(xr4, l0 + (uint32_t)(l * kThreads * 16), ((U + l) * kThreads + t) * 16);
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(T.x + wg0), (short)0, nv * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(T.q + wg0), (short)0, nv * 8, 0x00020000);
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 16, u * kThreads * 16, 0);
+    v[u] = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
+  wait_vm<0>();       // the DMA is not tracked by the compiler
+  __syncthreads();
+#pragma unroll
+  for (int l = 0; l < L; ++l) m = max(m, absmax8(lv[l][t]));
+  m = block_max_u32<kThreads>(m << 16, red);
+  uint32_t a = grid_max(T.gw, m, b, T.nblocks, sh);
+  if (a == kNoMax) {
+    a = 0;
+    for (int64_t i = t; i < T.nvec; i += kThreads) a = max(a, absmax8(T.x[i]) << 16);
+    a = block_max_u32<kThreads>(a, red);
+  }
+  const float am = __uint_as_float(a);
+  const float s = scale_from_amax<FMT>(am);
+  if (b == 0 && t == 0) {
+    *T.amax = am;
+    if (T.scale) *T.scale = s;
+    *T.scale_inv = 1.0f / s;
+  }
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const uint2 c = cast8<FMT>(u < U ? v[u % U] : lv[(u + L - U) % L][t], s);
+    u32x2_t w;
+    w[0] = c.x;
+    w[1] = c.y;
+    __builtin_amdgcn_raw_buffer_store_b64(w, qr, t * 8, u * kThreads * 8, 0);
+  }
+}
+
+// Current scaling of two tensors (a GEMM's two operands) in one launch:
+// workgroups 0 .. t[0].nblocks - 1 quantise the first tensor, the others the
+// second, each tensor with a grid-wide maximum of its own.  The grid is at
+// most what the device holds at once, like k_amax_cast's.
+template <int FA, int FB, int U, int L>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+k_amax_cast_pair(PairArgs a) {
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t sh;
+  __shared__ __attribute__((aligned(16))) uint4 lv[L][kThreads];
+  if (blockIdx.x < a.t[0].nblocks)
+    amax_cast_held<FA, U, L>(a.t[0], blockIdx.x, lv, red, &sh);
+  else
+    amax_cast_held<FB, U, L>(a.t[1], blockIdx.x - a.t[0].nblocks, lv, red, &sh);
 }
 
 // 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
@@ -1218,6 +1318,79 @@ hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, in
   else
     cast_kernels<kInF32>(x, rows, cols, fmt, src, q, qT, nullptr, g, s);
   return hipGetLastError();
+}
+
+// The paired launch: U = 24 vectors per thread in VGPRs, L = 8 in LDS.
+constexpr int kPairU = 24, kPairL = 8;
+
+template <int FA, int FB>
+static int pair_capacity() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, k_amax_cast_pair<FA, FB, kPairU, kPairL>, kThreads, 0) != hipSuccess)
+      per_cu = 0;
+    cached[dev] = per_cu > 0 ? per_cu * device_cu_count() : -1;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+template <int FA, int FB>
+static hipError_t try_pair(PairArgs& a, hipStream_t s, bool* done) {
+  constexpr int64_t per = (int64_t)(kPairU + kPairL) * kThreads;
+  int64_t g[2];
+  for (int i = 0; i < 2; ++i) {
+    g[i] = (a.t[i].nvec + per - 1) / per;
+    if (g[i] > kMaxPartials) return hipSuccess;
+    a.t[i].nblocks = (uint32_t)g[i];
+  }
+  if (g[0] + g[1] > pair_capacity<FA, FB>()) return hipSuccess;
+  hipLaunchKernelGGL((k_amax_cast_pair<FA, FB, kPairU, kPairL>), dim3((unsigned)(g[0] + g[1])),
+                     dim3(kThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) *done = true;
+  return err;
+}
+
+hipError_t launch_quantize_pair_current(const CurrentTensor& ta, const CurrentTensor& tb,
+                                        hipStream_t s) {
+  const int64_t na = ta.rows * ta.cols, nb = tb.rows * tb.cols;
+  if (na > 0 && nb > 0) {
+    uint32_t* part = nullptr;
+    hipError_t err = stream_partials(s, &part);
+    if (err != hipSuccess) return err;
+    PairArgs a;
+    const CurrentTensor* in[2] = {&ta, &tb};
+    for (int i = 0; i < 2; ++i) {
+      a.t[i].x = static_cast<const uint4*>(in[i]->x);
+      a.t[i].nvec = in[i]->rows * in[i]->cols / 8;
+      a.t[i].q = reinterpret_cast<uint2*>(in[i]->q);
+      a.t[i].gw = part + kWorkspaceWords + i * kGridSetWords;
+      a.t[i].amax = in[i]->amax;
+      a.t[i].scale = in[i]->scale;
+      a.t[i].scale_inv = in[i]->scale_inv;
+      a.t[i].nblocks = 0;
+    }
+    bool done = false;
+    if (ta.fmt == kE4M3 && tb.fmt == kE4M3)
+      err = try_pair<kE4M3, kE4M3>(a, s, &done);
+    else if (ta.fmt == kE4M3)
+      err = try_pair<kE4M3, kE5M2>(a, s, &done);
+    else if (tb.fmt == kE4M3)
+      err = try_pair<kE5M2, kE4M3>(a, s, &done);
+    else
+      err = try_pair<kE5M2, kE5M2>(a, s, &done);
+    if (err != hipSuccess || done) return err;
+  }
+  // an empty tensor, or a pair the device cannot hold at once: one call each
+  hipError_t err = launch_quantize_current(ta.x, ta.rows, ta.cols, ta.fmt, ta.q, nullptr, ta.amax,
+                                           ta.scale, ta.scale_inv, s, kInBF16);
+  if (err != hipSuccess) return err;
+  return launch_quantize_current(tb.x, tb.rows, tb.cols, tb.fmt, tb.q, nullptr, tb.amax, tb.scale,
+                                 tb.scale_inv, s, kInBF16);
 }
 
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s) {

@@ -38,7 +38,8 @@ class Operand(ctypes.Structure):
 
 
 _lib = None
-_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_quantize_tensor_current", "fp8_amax_f32",
+_EXPORTS = ["fp8_amax", "fp8_quantize_tensor", "fp8_quantize_tensor_current",
+            "fp8_quantize_pair_current", "fp8_amax_f32",
             "fp8_quantize_tensor_f32",
             "fp8_amax_history_update", "fp8_quantize_block",
             "fp8_quantize_mx", "fp8_quantize_block_t", "fp8_quantize_mx_t", "fp8_gemm_fprop",
@@ -61,6 +62,8 @@ def lib():
             "fp8_quantize_tensor": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_amax_f32": [vp, i64, i64, i32, vp, vp, vp, vp],
             "fp8_quantize_tensor_current": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
+            "fp8_quantize_pair_current": [vp, i64, i64, i32, vp, vp, vp, vp,
+                                          vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_quantize_tensor_f32": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_amax_history_update": [vp, i32, i64, vp, i32, vp, vp, vp],
             "fp8_quantize_block": [vp, i64, i64, i32, i32, i32, vp, vp, vp],
@@ -123,6 +126,17 @@ def fp8_quantize_tensor_current(x, fmt, q, qT, amax, scale, scale_inv, stream=No
            lib().fp8_quantize_tensor_current(_ptr(x), rows, cols, fmt, _ptr(q), _ptr(qT),
                                              _ptr(amax), _ptr(scale), _ptr(scale_inv),
                                              _stream(stream)))
+
+
+def fp8_quantize_pair_current(a, fmt_a, qa, amax_a, scale_a, scale_inv_a,
+                              b, fmt_b, qb, amax_b, scale_b, scale_inv_b, stream=None):
+    ra, ca = _rc(a)
+    rb, cb = _rc(b)
+    _check("fp8_quantize_pair_current",
+           lib().fp8_quantize_pair_current(_ptr(a), ra, ca, fmt_a, _ptr(qa), _ptr(amax_a),
+                                           _ptr(scale_a), _ptr(scale_inv_a),
+                                           _ptr(b), rb, cb, fmt_b, _ptr(qb), _ptr(amax_b),
+                                           _ptr(scale_b), _ptr(scale_inv_b), _stream(stream)))
 
 
 def fp8_amax_f32(x, fmt, amax, scale=None, scale_inv=None, stream=None):

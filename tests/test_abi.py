@@ -93,6 +93,23 @@ def test_quantize_current_errors(L):
     assert c(P, 4, 16, 2, P, None, P, None, P, None) == UNSUP
 
 
+def test_quantize_pair_current_errors(L):
+    c = L.fp8_quantize_pair_current
+    good = (P, 4, 16, 0, P, P, None, P)
+    assert c(P, 4, 16, 0, P, None, None, P, *good, None) == NULL        # a's amax
+    assert c(*good, P, 4, 16, 0, P, P, None, None, None) == NULL        # b's scale_inv
+    assert c(None, 4, 16, 0, P, P, None, P, *good, None) == NULL        # a's input
+    assert c(*good, P, 4, 16, 0, None, P, None, P, None) == NULL        # b's output
+    assert c(P, -1, 16, 0, P, P, None, P, *good, None) == SHAPE
+    assert c(*good, P, 4, 24, 0, P, P, None, P, None) == ALIGN          # b's cols % 16
+    assert c(PU, 4, 16, 0, P, P, None, P, *good, None) == ALIGN
+    assert c(*good, P, 4, 16, 0, P, P, PU, P, None) == ALIGN            # b's scale
+    assert c(P, 4, 16, 2, P, P, None, P, *good, None) == UNSUP
+    assert c(*good, P, 4, 16, 5, P, P, None, P, None) == UNSUP
+    # a is checked before b
+    assert c(P, 4, 16, 2, P, P, None, P, P, 4, 24, 0, P, P, None, P, None) == UNSUP
+
+
 def test_f32_input_errors(L):
     a = L.fp8_amax_f32
     assert a(P, 4, 16, 0, None, None, None, None) == NULL

@@ -210,6 +210,58 @@ def test_quantize_tensor_current_concurrent_streams(F, orc):
         assert np.array_equal(bytes8(q), wq)
 
 
+def _current_outputs(shape):
+    return (empty_dev(shape, torch.uint8),) + tuple(empty_dev(1, torch.float32) for _ in range(3))
+
+
+def _check_current(orc, x, fmt, q, am, s, si, label):
+    wa = orc.amax(x) if x.size else 0.0
+    ws, wsi = orc.scale_from_amax(wa, fmt)
+    assert f32(am)[0].view(np.uint32) == np.float32(wa).view(np.uint32), label
+    assert f32(s)[0] == ws and f32(si)[0] == wsi, label
+    if x.size:
+        wq, _, _ = orc.quantize_tensor(x, fmt, ws)
+        assert np.array_equal(bytes8(q), wq), label
+
+
+# (4096, 4096) + (11008, 4096): the LLaMA2-7B up-projection's X and W, one
+# launch; (8192, 8192) + (256, 256): more than the device holds at once, one
+# call per tensor; (0, 16): an empty tensor.
+@pytest.mark.parametrize("sa,sb,fa,fb", [
+    ((1, 16), (37, 48), E4M3, E5M2),
+    ((256, 256), (256, 256), E4M3, E4M3),
+    ((4112, 8208), (272, 384), E5M2, E4M3),
+    ((1000, 1008), (3000, 2064), E5M2, E5M2),
+    ((4096, 4096), (11008, 4096), E4M3, E4M3),
+    ((8192, 8192), (256, 256), E4M3, E4M3),
+    ((0, 16), (37, 48), E4M3, E4M3),
+])
+def test_quantize_pair_current(F, orc, sa, sb, fa, fb):
+    """Current scaling of two tensors in one call: each tensor's amax, scale
+    pair and FP8 bytes are the oracle's, bit for bit.  Three calls in a row on
+    one stream, the second with the tensors' data exchanged for fresh draws
+    (one with a NaN) and a single-tensor call in between, so each call starts
+    from the words the previous one left."""
+    outs = (_current_outputs(sa), _current_outputs(sb))
+    for rep in range(3):
+        xa = rand_bits(sa, 900 + 10 * rep + sa[1], 2.0, specials=True)
+        xb = rand_bits(sb, 901 + 10 * rep + sb[1], 0.02, specials=True)
+        if rep == 1 and xb.size:
+            xb.reshape(-1)[xb.size // 2] = 0x7FC0                      # NaN: amax NaN, scale 1
+        da = dev_bf16(xa) if xa.size else torch.empty(sa, dtype=torch.bfloat16, device=DEV)
+        db = dev_bf16(xb) if xb.size else torch.empty(sb, dtype=torch.bfloat16, device=DEV)
+        F.fp8_quantize_pair_current(da, fa, *outs[0], db, fb, *outs[1])
+        if rep == 1:
+            one = _current_outputs((64, 64))
+            x1 = rand_bits((64, 64), 77, 1.0)
+            F.fp8_quantize_tensor_current(dev_bf16(x1), E4M3, one[0], None, *one[1:])
+        torch.cuda.synchronize()
+        _check_current(orc, xa, fa, *outs[0], label=f"a rep {rep}")
+        _check_current(orc, xb, fb, *outs[1], label=f"b rep {rep}")
+        if rep == 1:
+            _check_current(orc, x1, E4M3, *one, label="single")
+
+
 def rand_f32(shape, seed, scale=1.0):
     """FP32 values with a wide magnitude range and a few specials."""
     rng = np.random.Generator(np.random.PCG64(seed))
