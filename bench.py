@@ -203,13 +203,13 @@ class Path:
             c("gemm wgrad", "mfma", gemm, F.fp8_gemm_wgrad, F.operand(self.gqT, E4, sg, self.gsT),
               F.operand(self.xqT, E4, sx, self.xsT), M, N, K, self.dw)
         elif r == "tensor":
-            # current scaling, one call per tensor: the amax and the cast in one
-            # launch with a grid-wide maximum, reading the BF16 tensor once and
-            # writing the FP8 copy (3 B/element, the least any pass can move)
-            c("amax+cast X", "hbm", 3 * M * K, F.fp8_quantize_tensor_current, self.x, F.E4M3,
-              self.xq, None, self.xa, self.xs, self.xsi)
-            c("amax+cast W", "hbm", 3 * N * K, F.fp8_quantize_tensor_current, self.w, F.E4M3,
-              self.wq, None, self.wa, self.ws, self.wsi)
+            # current scaling of both operands in one launch: each tensor's amax
+            # from a grid-wide maximum of its own, then its cast, reading each
+            # BF16 tensor once and writing its FP8 copy (3 B/element, the least
+            # any pass can move)
+            c("amax+cast X and W", "hbm", 3 * (M * K + N * K), F.fp8_quantize_pair_current,
+              self.x, F.E4M3, self.xq, self.xa, self.xs, self.xsi,
+              self.w, F.E4M3, self.wq, self.wa, self.ws, self.wsi)
             c("gemm fprop", "mfma", gemm, F.fp8_gemm_fprop,
               F.operand(self.xq, F.E4M3, F.SCALE_TENSOR, self.xsi),
               F.operand(self.wq, F.E4M3, F.SCALE_TENSOR, self.wsi), M, N, K, self.y)
