@@ -92,16 +92,40 @@ def quant_tensor_current_one_call(F, orc, t, fmt, label):
     return q, si, qh, f32(si)
 
 
-# tiny case: the two-call sequence; LLaMA2-7B up-projection: the one-call
-# current scaling the benchmark times
-@pytest.mark.parametrize("key", ["c1", "c2"])
-def test_per_tensor_current_fprop(F, orc, key):
+def quant_pair_current(F, orc, x, w, fmt, label):
+    """fp8_quantize_pair_current of X and W (the benchmark's call), each
+    checked bit-exactly; returns the quant_tensor_current tuple per tensor."""
+    outs = [(empty(t.shape, torch.uint8),) + tuple(empty(1, torch.float32) for _ in range(3))
+            for t in (x, w)]
+    F.fp8_quantize_pair_current(x, fmt, *outs[0], w, fmt, *outs[1])
+    res = []
+    for t, (q, am, s, si), name in zip((x, w), outs, ("X", "W")):
+        tb = bits16(t)
+        wa = orc.amax(tb)
+        ws, wsi = orc.scale_from_amax(wa, fmt)
+        assert f32(am)[0].view(np.uint32) == np.float32(wa).view(np.uint32), f"{label} {name} amax"
+        assert f32(s)[0] == ws and f32(si)[0] == wsi, f"{label} {name} scale"
+        wq, _, _ = orc.quantize_tensor(tb, fmt, ws)
+        qh = bytes8(q)
+        assert np.array_equal(qh, wq), f"{label} {name} bytes"
+        res.append((q, si, qh, f32(si)))
+    return res
+
+
+# tiny case: the two-call sequence; LLaMA2-7B up-projection: X and W in one
+# launch (the call the benchmark times), and the one-call current scaling of
+# each tensor
+@pytest.mark.parametrize("key,calls", [("c1", "two"), ("c2", "pair"), ("c2", "one")])
+def test_per_tensor_current_fprop(F, orc, key, calls):
     cfg = gen.CONFIGS[key]
     x = gen.make_x(cfg, DEV)
     w = gen.make_w(cfg, DEV)
-    quant = quant_tensor_current if key == "c1" else quant_tensor_current_one_call
-    xq, xsi, xh, xs = quant(F, orc, x, E4M3, f"{key} X")
-    wq, wsi, wh, ws = quant(F, orc, w, E4M3, f"{key} W")
+    if calls == "pair":
+        (xq, xsi, xh, xs), (wq, wsi, wh, ws) = quant_pair_current(F, orc, x, w, E4M3, key)
+    else:
+        quant = quant_tensor_current if calls == "two" else quant_tensor_current_one_call
+        xq, xsi, xh, xs = quant(F, orc, x, E4M3, f"{key} X")
+        wq, wsi, wh, ws = quant(F, orc, w, E4M3, f"{key} W")
     y = empty((cfg.M, cfg.N), torch.bfloat16)
     F.fp8_gemm_fprop(F.operand(xq, E4M3, T, xsi), F.operand(wq, E4M3, T, wsi),
                      cfg.M, cfg.N, cfg.K, y)

@@ -1,5 +1,6 @@
 """A whole per-tensor current-scaling step (one-launch amax+cast of X and W,
-then fprop) captured in a HIP graph and replayed.  The one-launch cast keeps a
+one launch per tensor or both in one, then fprop) captured in a HIP graph and
+replayed.  The one-launch cast keeps a
 generation number and counters in the per-stream workspace between calls, so
 replays must leave them consistent: every replay's FP8 bytes, scales and BF16
 output equal the eager step's bit for bit, with unrelated eager work on the
@@ -25,7 +26,8 @@ def F():
     return fp8sg
 
 
-def test_graph_replay_current_scaling_step(F):
+@pytest.mark.parametrize("calls", ["one", "pair"])
+def test_graph_replay_current_scaling_step(F, calls):
     cfg = gen.CONFIGS["c2"]
     M, K, N = 1024, cfg.K, 2048
     x = gen.make_x(cfg, DEV, M=M)
@@ -39,8 +41,12 @@ def test_graph_replay_current_scaling_step(F):
                     **{k: torch.empty(1, device=DEV) for k in ("xa", "xs", "xsi", "wa", "ws", "wsi")})
 
     def step(b):
-        F.fp8_quantize_tensor_current(x, E4M3, b["xq"], None, b["xa"], b["xs"], b["xsi"])
-        F.fp8_quantize_tensor_current(w, E4M3, b["wq"], None, b["wa"], b["ws"], b["wsi"])
+        if calls == "pair":
+            F.fp8_quantize_pair_current(x, E4M3, b["xq"], b["xa"], b["xs"], b["xsi"],
+                                        w, E4M3, b["wq"], b["wa"], b["ws"], b["wsi"])
+        else:
+            F.fp8_quantize_tensor_current(x, E4M3, b["xq"], None, b["xa"], b["xs"], b["xsi"])
+            F.fp8_quantize_tensor_current(w, E4M3, b["wq"], None, b["wa"], b["ws"], b["wsi"])
         F.fp8_gemm_fprop(F.operand(b["xq"], E4M3, F.SCALE_TENSOR, b["xsi"]),
                          F.operand(b["wq"], E4M3, F.SCALE_TENSOR, b["wsi"]), M, N, K, b["y"])
 
