@@ -203,7 +203,9 @@ fp8_status_t fp8_amax_history_update(float* history, int32_t history_len, int64_
  *   q           out uint8 [rows][cols]
  *   scale_inv   out float [rows/block_rows][cols/128]
  * Both FP8 formats are accepted (the pages use E4M3).
- * Errors: NULL; sizes; block shape; alignment; fmt. */
+ * Errors: NULL; sizes; a block shape other than 1x128 / 128x128 or an unknown
+ * fmt (FP8_ERR_UNSUPPORTED); cols % 128 or rows % block_rows (FP8_ERR_SHAPE);
+ * alignment. */
 fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                 int32_t block_rows, int32_t block_cols, uint8_t* q,
                                 float* scale_inv, void* stream);
@@ -216,6 +218,7 @@ fp8_status_t fp8_quantize_block(const void* x_bf16, int64_t rows, int64_t cols, 
  *   x_bf16     [rows][cols] BF16, cols % 32 == 0
  *   q          out uint8 [rows][cols]
  *   scale_e8m0 out uint8 [rows][cols/32]
+ * Both FP8 formats are accepted (the MXFP8 workloads use E4M3).
  * Errors: NULL; sizes; alignment; fmt. */
 fp8_status_t fp8_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                              uint8_t* q, uint8_t* scale_e8m0, void* stream);

@@ -13,6 +13,7 @@
 // finalize kernel reduces them; same-address device atomics from thousands of
 // workgroups serialise (about 10 ns each on MI355X) and would cost more than
 // the pass itself.
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -1136,17 +1137,17 @@ hipError_t stream_partials(hipStream_t s, uint32_t** out) {
 }
 
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];   // per device; 0 = not known yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cached[dev].load(std::memory_order_relaxed);
 }
 
 #define FP8SG_FMT_DISPATCH(fmt, ...)                   \
@@ -1243,17 +1244,18 @@ hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int
 // (0 if unknown), cached per device.
 template <int FMT, int U>
 static int coop_capacity() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];   // per device; 0 = not known yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_amax_cast<FMT, U>, kThreads, 0) !=
         hipSuccess)
       per_cu = 0;
-    cached[dev] = per_cu > 0 ? per_cu * device_cu_count() : -1;
+    cached[dev].store(per_cu > 0 ? per_cu * device_cu_count() : -1, std::memory_order_relaxed);
   }
-  return cached[dev] > 0 ? cached[dev] : 0;
+  const int c = cached[dev].load(std::memory_order_relaxed);
+  return c > 0 ? c : 0;
 }
 
 // One launch of k_amax_cast<FMT, U> if nvec vectors fit a grid the device
@@ -1325,17 +1327,18 @@ constexpr int kPairU = 24, kPairL = 8;
 
 template <int FA, int FB>
 static int pair_capacity() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];   // per device; 0 = not known yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, k_amax_cast_pair<FA, FB, kPairU, kPairL>, kThreads, 0) != hipSuccess)
       per_cu = 0;
-    cached[dev] = per_cu > 0 ? per_cu * device_cu_count() : -1;
+    cached[dev].store(per_cu > 0 ? per_cu * device_cu_count() : -1, std::memory_order_relaxed);
   }
-  return cached[dev] > 0 ? cached[dev] : 0;
+  const int c = cached[dev].load(std::memory_order_relaxed);
+  return c > 0 ? c : 0;
 }
 
 template <int FA, int FB>

@@ -186,3 +186,23 @@ def test_convert_errors(L):
     assert c(P, -1, 0, P, None) == SHAPE
     assert c(P, 4, 3, P, None) == UNSUP
     assert c(PU, 4, 0, P, None) == ALIGN
+
+
+def test_plain_c_caller(tmp_path):
+    """A C99 program (tests/c_abi_check.c) includes the header with no HIP or
+    torch headers, links the library and gets the documented statuses from
+    its validation, before anything reaches a device."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    lib_dir = os.path.join(ROOT, "scaled_fp8_gemm_amd")
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.check_call([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror",
+                           "-I", os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "tests", "c_abi_check.c"),
+                           "-L", lib_dir, "-lfp8sg", f"-Wl,-rpath,{lib_dir}", "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout
