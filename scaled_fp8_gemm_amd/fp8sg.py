@@ -187,7 +187,12 @@ def fp8_quantize_mx_t(x, fmt, q, scale_e8m0, qT, scale_e8m0_T, stream=None):
 
 
 def operand(data, fmt, scaling, scale_inv) -> Operand:
-    return Operand(_ptr(data), fmt, scaling, _ptr(scale_inv))
+    """The operand holds the two tensors as well as their addresses, so that
+    temporaries passed here stay allocated until the GEMM call has been
+    enqueued (after that, torch's stream-ordered reuse is safe)."""
+    o = Operand(_ptr(data), fmt, scaling, _ptr(scale_inv))
+    o._tensors = (data, scale_inv)
+    return o
 
 
 def fp8_gemm_fprop(x: Operand, w: Operand, M, N, K, y, stream=None):

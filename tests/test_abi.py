@@ -206,3 +206,24 @@ def test_plain_c_caller(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
+
+
+def test_operand_keeps_its_tensors():
+    """fp8sg.operand holds the tensors it points at, so temporaries passed to
+    it (say operand(torch.from_numpy(a).to(dev), ...)) are not freed, and
+    their memory reused, before the GEMM call is enqueued."""
+    import gc
+    import weakref
+
+    import torch
+    from scaled_fp8_gemm_amd import fp8sg
+    data, scale = torch.zeros(64, dtype=torch.uint8), torch.ones(1)
+    refs = (weakref.ref(data), weakref.ref(scale))
+    o = fp8sg.operand(data, fp8sg.E4M3, fp8sg.SCALE_TENSOR, scale)
+    del data, scale
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert o.data == refs[0]().data_ptr() and o.scale_inv == refs[1]().data_ptr()
+    del o
+    gc.collect()
+    assert all(r() is None for r in refs)

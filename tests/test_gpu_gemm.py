@@ -311,3 +311,33 @@ def test_fprop_fused_next_layer_quantise(F, orc, scaling, yfmt):
         mode = {"tensor": 0, "block": 1}[scaling]
         check_gemm(orc, yb, A, B, E4M3, E4M3, mode, sa, sb, 1, 128 if scaling == "block" else 1,
                    label=f"fused {scaling}")
+
+
+def test_gemm_at_the_contraction_limit(F, orc):
+    """Maximum size: K = 2^23, the largest contraction the GEMM accepts (a
+    256-row operand tile then spans 2^31 bytes, the edge of the kernels'
+    32-bit buffer offsets).  One 256 x 256 tile of random E4M3 codes of
+    magnitude 0.5 .. 7.5 (a quantised tensor's spread; full-range codes would
+    let the instruction's truncation reach 1 % over 65536 steps); sampled
+    outputs, including all four corners, against the oracle's FP64 values:
+    the MFMA error bound, max-relative <= 1e-2 and p99 <= 2 BF16 ulp."""
+    from tests.gpu_helpers import compare, entries_reference
+    M = N = 256
+    K = 1 << 23
+    rng = np.random.Generator(np.random.PCG64(223))
+
+    def codes(rows):
+        c = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)
+        # random sign and mantissa, exponent field 6 .. 9 (no NaN codes)
+        return (c & 0x87) | ((((c >> 3) & 3) + 6) << 3).astype(np.uint8)
+
+    A, B = codes(M), codes(N)
+    sa, sb = np.float32([0.5]), np.float32([0.25])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(F.operand(dev_u8(A), E4M3, TENSOR, dev_f32(sa)),
+                     F.operand(dev_u8(B), E4M3, TENSOR, dev_f32(sb)), M, N, K, y)
+    torch.cuda.synchronize()
+    ii = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, 28)]).astype(np.int64)
+    jj = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 28)]).astype(np.int64)
+    val, absd, T, S = entries_reference(orc, A, B, E4M3, E4M3, 0, sa, sb, ii, jj, chunk=4)
+    compare(orc, bits16(y)[ii, jj], val, absd, T, S, label="K = 2^23", realistic=True)

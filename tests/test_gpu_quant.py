@@ -413,3 +413,55 @@ def test_convert_every_fp32_pattern(F, orc, fmt):
     q = empty_dev(7, torch.uint8)
     F.fp8_convert_f32(x, fmt, q)
     assert np.array_equal(bytes8(q), orc.encode(x.cpu().numpy(), fmt))
+
+
+def test_quantise_beyond_2_31_elements(F, orc):
+    """Maximum sizes: a BF16 tensor of 65552 x 32768 = 2^31 + 2^19 elements
+    (4.3 GB), so element indices and byte offsets pass 2^31.  Current scaling
+    (two launches at this size), the transposed copy, 1x128 blocks and MX
+    blocks are each the oracle's, bit for bit; the largest magnitude sits
+    beyond element 2^31."""
+    R, C = 65552, 32768
+    n = R * C
+    rng = np.random.Generator(np.random.PCG64(31))
+    x = rng.integers(0, 2 ** 32, size=n // 2, dtype=np.uint32).view(np.uint16)
+    x &= 0xBFFF                                  # |x| < 2: finite, with subnormals
+    x[(1 << 31) + 12345] = 0x4120                # 10.0, the amax, past 2^31
+    x = x.reshape(R, C)
+    xd = dev_bf16(x)
+    fmt = E4M3
+
+    am, s, si = (empty_dev(1, torch.float32) for _ in range(3))
+    q = empty_dev((R, C), torch.uint8)
+    F.fp8_quantize_tensor_current(xd, fmt, q, None, am, s, si)
+    torch.cuda.synchronize()
+    wa = orc.amax(x)
+    assert wa == 10.0
+    ws, wsi = orc.scale_from_amax(wa, fmt)
+    assert f32(am)[0] == wa and f32(s)[0] == ws and f32(si)[0] == wsi
+    wq, wqT, _ = orc.quantize_tensor(x, fmt, ws, transposed=True)
+    assert np.array_equal(bytes8(q), wq)
+
+    qT = empty_dev((C, R), torch.uint8)
+    q.zero_()
+    F.fp8_quantize_tensor(xd, fmt, s, q, qT)
+    torch.cuda.synchronize()
+    assert np.array_equal(bytes8(q), wq)
+    del wq
+    assert np.array_equal(bytes8(qT), wqT)
+    del wqT, qT
+
+    sb = empty_dev((R, C // 128), torch.float32)
+    F.fp8_quantize_block(xd, fmt, 1, 128, q, sb)
+    torch.cuda.synchronize()
+    bq, bs = orc.quantize_block(x, fmt, 1, 128)
+    assert np.array_equal(f32(sb).view(np.uint32), bs.view(np.uint32))
+    assert np.array_equal(bytes8(q), bq)
+    del bq, bs, sb
+
+    e = empty_dev((R, C // 32), torch.uint8)
+    F.fp8_quantize_mx(xd, fmt, q, e)
+    torch.cuda.synchronize()
+    mq, me = orc.quantize_mx(x, fmt)
+    assert np.array_equal(bytes8(e), me)
+    assert np.array_equal(bytes8(q), mq)
