@@ -341,3 +341,47 @@ def test_gemm_at_the_contraction_limit(F, orc):
     jj = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 28)]).astype(np.int64)
     val, absd, T, S = entries_reference(orc, A, B, E4M3, E4M3, 0, sa, sb, ii, jj, chunk=4)
     compare(orc, bits16(y)[ii, jj], val, absd, T, S, label="K = 2^23", realistic=True)
+
+
+def test_gemm_output_beyond_2_31_elements(F, orc):
+    """Maximum size: Y of 65792 x 32768 = 2^31 + 2^23 elements (4.3 GB of
+    BF16), K = 128, so output offsets pass 2^31.  Sampled outputs (the last
+    rows included) against the oracle within the MFMA bound; then the fused
+    epilogue at the same size: its BF16 output equals the plain call's bit for
+    bit, and its FP8 copy and amax equal the oracle's cast and amax of that
+    output."""
+    from tests.gpu_helpers import compare, entries_reference
+    M, N, K = 65792, 32768, 128
+    rng = np.random.Generator(np.random.PCG64(231))
+
+    def codes(rows):
+        c = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)
+        return (c & 0x87) | ((((c >> 3) & 3) + 6) << 3).astype(np.uint8)
+
+    A, B = codes(M), codes(N)
+    sa, sb = np.float32([0.5]), np.float32([0.25])
+    oa = F.operand(dev_u8(A), E4M3, TENSOR, dev_f32(sa))
+    ob = F.operand(dev_u8(B), E4M3, TENSOR, dev_f32(sb))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm_fprop(oa, ob, M, N, K, y)
+    ii = np.concatenate([np.full(64, M - 1), rng.integers(M - 256, M, 64),
+                         rng.integers(0, M, 128)]).astype(np.int64)
+    jj = np.concatenate([rng.integers(0, N, 64), np.full(64, N - 1),
+                         rng.integers(0, N, 128)]).astype(np.int64)
+    g = bits16(y[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)])
+    val, absd, T, S = entries_reference(orc, A, B, E4M3, E4M3, 0, sa, sb, ii, jj)
+    compare(orc, g, val, absd, T, S, label="Y > 2^31 elements", realistic=True)
+
+    yf = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    yq = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+    am = torch.empty(1, dtype=torch.float32, device=DEV)
+    ys = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    F.fp8_gemm_fprop_fused(oa, ob, M, N, K, yf, E4M3, ys, yq, am)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(yf.view(torch.int16), y.view(torch.int16)))
+    del yf
+    yb = bits16(y)
+    del y
+    wq, _, wam = orc.quantize_tensor(yb, E4M3, f32(ys)[0], want_amax=True)
+    assert f32(am)[0].view(np.uint32) == np.float32(wam).view(np.uint32)
+    assert np.array_equal(bytes8(yq), wq)
