@@ -338,58 +338,6 @@ __device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t b
   return *sh;
 }
 
-template <int FMT, int U>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
-    const uint4* __restrict__ x, int64_t nvec, uint2* __restrict__ q, uint32_t* __restrict__ gw,
-    float* __restrict__ amax, float* __restrict__ scale, float* __restrict__ scale_inv) {
-  __shared__ uint32_t red[kThreads / 64];
-  __shared__ uint32_t sh;
-  // This workgroup's vectors through buffer descriptors covering exactly
-  // them: one 32-bit lane offset in a VGPR, the vector's offset in an SGPR,
-  // and the range check instead of predication (loads past the end read 0,
-  // stores past it are dropped).
-  const int64_t wg0 = (int64_t)blockIdx.x * (U * kThreads);
-  const int nv = (int)min<int64_t>(nvec - wg0, (int64_t)U * kThreads);   // this workgroup's vectors
-  const int t = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(x + wg0), (short)0, nv * 16, 0x00020000);
-  const __amdgpu_buffer_rsrc_t qr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(q + wg0), (short)0, nv * 8, 0x00020000);
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  uint4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(xr, t * 16, u * kThreads * 16, 0);
-    v[u] = make_uint4(r[0], r[1], r[2], r[3]);
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
-  m = block_max_u32<kThreads>(m << 16, red);
-  uint32_t a = grid_max(gw, m, blockIdx.x, gridDim.x, &sh);
-  if (a == kNoMax) {
-    a = 0;
-    for (int64_t i = t; i < nvec; i += kThreads) a = max(a, absmax8(x[i]) << 16);
-    a = block_max_u32<kThreads>(a, red);
-  }
-  const float am = __uint_as_float(a);
-  const float s = scale_from_amax<FMT>(am);
-  if (blockIdx.x == 0 && t == 0) {
-    *amax = am;
-    if (scale) *scale = s;
-    *scale_inv = 1.0f / s;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint2 c = cast8<FMT>(v[u], s);
-    u32x2_t w;
-    w[0] = c.x;
-    w[1] = c.y;
-    __builtin_amdgcn_raw_buffer_store_b64(w, qr, t * 8, u * kThreads * 8, 0);
-  }
-}
-
 // One tensor of the paired current-scaling launch.
 struct PairTensor {
   const uint4* x;       // BF16 input, 16-byte vectors
@@ -424,11 +372,13 @@ __device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
   const int t = threadIdx.x;
   // LDS share first (vectors U .. V-1): lane i of a wave lands at m0 + 16 i,
   // i.e. at lv[l][t]; reads past the range give zeros
-  const v4i xr4 = make_rsrc(T.x + wg0, (uint32_t)nv * 16u);
-  const uint32_t l0 = lds_addr(&lv[0][t & ~63]);
+  if constexpr (L > 0) {
+    const v4i xr4 = make_rsrc(T.x + wg0, (uint32_t)nv * 16u);
+    const uint32_t l0 = lds_addr(&lv[0][t & ~63]);
 #pragma unroll
-  for (int l = 0; l < L; ++l)
-    dma16(xr4, l0 + (uint32_t)(l * kThreads * 16), ((U + l) * kThreads + t) * 16);
+    for (int l = 0; l < L; ++l)
+      dma16(xr4, l0 + (uint32_t)(l * kThreads * 16), ((U + l) * kThreads + t) * 16);
+  }
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(T.x + wg0), (short)0, nv * 16, 0x00020000);
   const __amdgpu_buffer_rsrc_t qr =
@@ -443,10 +393,12 @@ __device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
   uint32_t m = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) m = max(m, absmax8(v[u]));
-  wait_vm<0>();       // the DMA is not tracked by the compiler
-  __syncthreads();
+  if constexpr (L > 0) {
+    wait_vm<0>();     // the DMA is not tracked by the compiler
+    __syncthreads();
 #pragma unroll
-  for (int l = 0; l < L; ++l) m = max(m, absmax8(lv[l][t]));
+    for (int l = 0; l < L; ++l) m = max(m, absmax8(lv[l][t]));
+  }
   m = block_max_u32<kThreads>(m << 16, red);
   uint32_t a = grid_max(T.gw, m, b, T.nblocks, sh);
   if (a == kNoMax) {
@@ -461,13 +413,18 @@ __device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
     if (T.scale) *T.scale = s;
     *T.scale_inv = 1.0f / s;
   }
-#pragma unroll
-  for (int u = 0; u < V; ++u) {
-    const uint2 c = cast8<FMT>(u < U ? v[u % U] : lv[(u + L - U) % L][t], s);
+  auto store = [&](uint4 x8, int u) {
+    const uint2 c = cast8<FMT>(x8, s);
     u32x2_t w;
     w[0] = c.x;
     w[1] = c.y;
     __builtin_amdgcn_raw_buffer_store_b64(w, qr, t * 8, u * kThreads * 8, 0);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) store(v[u], u);
+  if constexpr (L > 0) {
+#pragma unroll
+    for (int l = 0; l < L; ++l) store(lv[l][t], U + l);
   }
 }
 
@@ -485,6 +442,19 @@ k_amax_cast_pair(PairArgs a) {
     amax_cast_held<FA, U, L>(a.t[0], blockIdx.x, lv, red, &sh);
   else
     amax_cast_held<FB, U, L>(a.t[1], blockIdx.x - a.t[0].nblocks, lv, red, &sh);
+}
+
+// Current scaling in one launch of one tensor: the body above with every
+// vector in VGPRs (U = 16 or 24, no LDS share), all workgroups on the tensor.
+template <int FMT, int U>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
+    const uint4* __restrict__ x, int64_t nvec, uint2* __restrict__ q, uint32_t* __restrict__ gw,
+    float* __restrict__ amax, float* __restrict__ scale, float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t sh;
+  const PairTensor T{x, nvec, q, gw, amax, scale, scale_inv, gridDim.x};
+  amax_cast_held<FMT, U, 0>(T, blockIdx.x, nullptr, red, &sh);
 }
 
 // 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
