@@ -1155,6 +1155,27 @@ hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* sc
   return hipGetLastError();
 }
 
+// Workgroups of k_cast_t the current device holds at once (at most the
+// partial buffer), cached per device: its grid-stride tile loop then runs
+// on a grid that is all resident (on the LLaMA2-13B-width X, 2560 tiles:
+// 38.0 instead of 39.7 us with a grid of 2048).
+template <int IN>
+static int cast_t_capacity() {
+  static std::atomic<int> cached[64];   // per device; 0 = not known yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxPartials;
+  if (cached[dev].load(std::memory_order_relaxed) == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_cast_t<kE4M3, true, IN>, kThreads,
+                                                     0) != hipSuccess)
+      per_cu = 0;
+    const int cap = per_cu * device_cu_count();
+    cached[dev].store(cap >= 1 && cap <= kMaxPartials ? cap : kMaxPartials,
+                      std::memory_order_relaxed);
+  }
+  return cached[dev].load(std::memory_order_relaxed);
+}
+
 template <int IN>
 static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
                          uint8_t* q, uint8_t* qT, uint32_t* part, int& g, hipStream_t s) {
@@ -1164,6 +1185,8 @@ static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, Sca
     const int64_t ntx = (cols + 127) / 128;
     const int64_t ntiles = ntx * ((rows + 127) / 128);
     g = grid_for(ntiles, 1);
+    const int cap = cast_t_capacity<IN>();
+    if (g > cap) g = cap;
     FP8SG_FMT_DISPATCH(fmt, {
       if (part)
         hipLaunchKernelGGL((k_cast_t<F, true, IN>), dim3(g), dim3(kThreads), 0, s, xb, rows, cols,
