@@ -1436,7 +1436,10 @@ hipError_t launch_quantize_t(const void* x, int64_t rows, int64_t cols, int fmt,
   if (rows * cols == 0) return hipSuccess;
   const int64_t ntx = (cols + 127) / 128;
   const int64_t ntiles = ntx * ((rows + 127) / 128);
-  const int g = grid_for(ntiles, 1);
+  // one tile per workgroup, the hardware dispatcher balancing them (on the
+  // GPT-175B MX weight's 36864 tiles: 512 instead of 562 us with a grid of
+  // 2048 workgroups walking them)
+  const int g = (int)(ntiles < (1 << 30) ? ntiles : (1 << 30));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   FP8SG_FMT_DISPATCH(fmt, {
     if (kind == kTBlock1)
