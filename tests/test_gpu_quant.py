@@ -465,3 +465,25 @@ def test_quantise_beyond_2_31_elements(F, orc):
     mq, me = orc.quantize_mx(x, fmt)
     assert np.array_equal(bytes8(e), me)
     assert np.array_equal(bytes8(q), mq)
+
+
+def test_quantize_pair_current_concurrent_streams(F, orc):
+    """Two paired one-launch calls running at once on different streams, each
+    grid as large as the device holds (the LLaMA2-7B up-projection's X and W):
+    however the grids interleave, every tensor's amax, scale pair and bytes
+    are the oracle's (a workgroup whose grid-wide wait runs out reduces its
+    tensor itself)."""
+    shapes = ((4096, 4096), (11008, 4096))
+    xs = [[rand_bits(sh, 800 + 10 * i + j, 2.0 if j == 0 else 0.02) for j, sh in enumerate(shapes)]
+          for i in range(2)]
+    dx = [[dev_bf16(x) for x in pair] for pair in xs]
+    outs = [[_current_outputs(sh) for sh in shapes] for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for d, o, st in zip(dx, outs, streams):
+            F.fp8_quantize_pair_current(d[0], E4M3, *o[0], d[1], E4M3, *o[1], stream=st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for j in range(2):
+            _check_current(orc, xs[i][j], E4M3, *outs[i][j], label=f"stream {i} tensor {j}")
