@@ -20,18 +20,20 @@
  *
  * Conventions for every call
  *   Memory      Every pointer argument except `stream` is device memory owned by
- *               the caller.  Tensors are dense and row-major.  The calls that
- *               produce an amax (fp8_amax*, fp8_quantize_tensor* with amax_out,
- *               fp8_quantize_tensor_current, fp8_quantize_pair_current,
- *               fp8_gemm_fprop_fused with y_amax) reduce through a 289 KB
- *               workspace (256 KB of partial maxima, 33 KB of grid-wide
- *               maximum words) that the library allocates (hipMalloc, and
- *               clears the maximum words on the stream) on the first such
- *               call on each (device, stream) pair and keeps until the
- *               process ends; calls on one stream run in order and share it,
- *               calls on different streams never do.  That first call must
- *               not be made under stream capture.  If the allocation fails
- *               the call returns FP8_ERR_HIP.  No other call allocates.
+ *               the caller.  Tensors are dense and row-major.  The library
+ *               allocates nothing and keeps no state between calls.
+ *   Workspace   The calls that produce an amax (fp8_amax*, fp8_quantize_tensor*
+ *               with amax_out, fp8_quantize_tensor_current,
+ *               fp8_quantize_pair_current, fp8_gemm_fprop_fused with y_amax)
+ *               reduce through a caller-owned device workspace of
+ *               FP8_WORKSPACE_BYTES, 256-byte aligned: partial maxima, and
+ *               the counters and flags of the one-launch grid-wide maximum.
+ *               Before its first use it must be zero-filled (any zero fill,
+ *               or fp8_workspace_init); every call leaves it ready for the
+ *               next.  Calls that may run at the same time (on different
+ *               streams, or graph replays on different streams) must use
+ *               different workspaces; calls ordered on one stream may share
+ *               one.  A graph captures the workspace address it was given.
  *   Stream      `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *               enqueue kernels and return; nothing synchronises.  Outputs are
  *               valid once the stream has passed the call.
@@ -66,6 +68,13 @@
 extern "C" {
 #endif
 
+/* Size in bytes of the workspace of the amax-producing calls (see Workspace):
+ * 65536 words of partial maxima (one per workgroup of a quantise launch, at
+ * most 2048, or one per 256x256 output tile of the fused GEMM epilogue),
+ * 8320 words of grid-wide maximum counters, maxima and flags (two sets of 65
+ * cache lines), and one 128-byte line of settings. */
+#define FP8_WORKSPACE_BYTES 295552
+
 typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format_t;
 
 typedef enum {
@@ -93,15 +102,29 @@ typedef struct {
   const void* scale_inv;   /* layout per fp8_scaling_t above */
 } fp8_operand_t;
 
+/* Prepare a workspace (FP8_WORKSPACE_BYTES, 256-byte aligned) for first
+ * use: zero-fills it with a kernel on `stream` (no memset, so the call may be
+ * captured in a graph) and sets the bound on the grid-wide wait of the
+ * one-launch current scaling.
+ *   wait_polls  0: the default bound (2^15 polls, several milliseconds);
+ *               n > 0: n polls.  A workgroup whose wait runs out reduces the
+ *               whole input itself, so results never change, only speed;
+ *               1 makes that slow path the common one (for tests).
+ * Errors: NULL workspace; wait_polls < 0 (FP8_ERR_SHAPE); alignment. */
+fp8_status_t fp8_workspace_init(void* workspace, int32_t wait_polls, void* stream);
+
 /* amax of a BF16 tensor and, optionally, the scale pair it implies.
  * [colossal] real-time scaling / [guide] just-in-time scaling: the scale comes
  * from the maximum of the tensor being cast.
  *   x_bf16     [rows][cols] BF16, 16-byte aligned (any rows, cols >= 0)
  *   amax       out float[1]
  *   scale, scale_inv   out float[1] each, nullable (scale rule above)
- * Errors: NULL x/amax; negative sizes; misaligned x; fmt not E4M3/E5M2. */
+ *   workspace  see Workspace
+ * Errors: NULL x/amax/workspace; negative sizes; misaligned x or workspace;
+ * fmt not E4M3/E5M2. */
 fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
-                      float* amax, float* scale, float* scale_inv, void* stream);
+                      float* amax, float* scale, float* scale_inv, void* workspace,
+                      void* stream);
 
 /* Per-tensor cast q = cast(x * scale[0]).  [guide] code changes: the GEMM
  * inputs are quantised; the transposed copy qT is the K-contiguous operand the
@@ -113,10 +136,12 @@ fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fm
  *   amax_out out float[1], nullable: amax of x, fused into the same pass
  *            (delayed scaling records it in its history; [colossal] delayed
  *            scaling fuses the scale update with the GEMM pipeline)
- * Errors: NULL x/scale/q; negative sizes; alignment; fmt. */
+ *   workspace  see Workspace; needed with amax_out, else may be NULL
+ * Errors: NULL x/scale/q (or workspace with amax_out); negative sizes;
+ * alignment; fmt. */
 fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                 void* stream);
+                                 void* workspace, void* stream);
 
 /* Per-tensor current scaling in one call: amax -> scale pair -> cast, the
  * sequence fp8_amax + fp8_quantize_tensor with identical results
@@ -136,11 +161,12 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
  *              (rows % 16 == 0)
  *   amax       out float[1];  scale  out float[1], nullable;
  *   scale_inv  out float[1]
- * Uses the workspace described under Memory.  Errors as fp8_amax and
- * fp8_quantize_tensor. */
+ *   workspace  see Workspace (the one-launch wait's bound is set there)
+ * Errors as fp8_amax and fp8_quantize_tensor. */
 fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64_t cols,
                                          int32_t fmt, uint8_t* q, uint8_t* qT, float* amax,
-                                         float* scale, float* scale_inv, void* stream);
+                                         float* scale, float* scale_inv, void* workspace,
+                                         void* stream);
 
 /* Per-tensor current scaling of a GEMM's two operands (for instance X and W
  * of fprop) in one call: the results are exactly those of
@@ -158,27 +184,28 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
  *   a_amax, a_scale, a_scale_inv, b_amax, ...   out float[1] each; the scale
  *                    pointers are nullable
  * The two tensors' outputs must not overlap each other or either input.
- * Uses the workspace described under Memory.  Errors as
- * fp8_quantize_tensor_current, checked for a, then for b, before any launch. */
+ *   workspace        see Workspace (one for both tensors)
+ * Errors as fp8_quantize_tensor_current, checked for a, then for b, before
+ * any launch. */
 fp8_status_t fp8_quantize_pair_current(const void* a_bf16, int64_t a_rows, int64_t a_cols,
                                        int32_t a_fmt, uint8_t* a_q, float* a_amax,
                                        float* a_scale, float* a_scale_inv, const void* b_bf16,
                                        int64_t b_rows, int64_t b_cols, int32_t b_fmt,
                                        uint8_t* b_q, float* b_amax, float* b_scale,
-                                       float* b_scale_inv, void* stream);
+                                       float* b_scale_inv, void* workspace, void* stream);
 
 /* FP32 master-weight input.  [snippets] forward-pass snippet: the master
  * weights are FP32 and are quantised to FP8 for the GEMM.  The same calls as
  * fp8_amax and fp8_quantize_tensor for an FP32 tensor: amax is the largest
  * |x| under NaN > inf > finite on the FP32 magnitude bits (exactly an FP32
  * value); the cast is sat_rne(fl32(x * scale)).  Shapes, alignment (16-byte
- * data) and errors as for the BF16 calls; the workspace note under Memory
- * applies to fp8_amax_f32 and to fp8_quantize_tensor_f32 with amax_out. */
+ * data), the workspace and errors as for the BF16 calls. */
 fp8_status_t fp8_amax_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
-                          float* amax, float* scale, float* scale_inv, void* stream);
+                          float* amax, float* scale, float* scale_inv, void* workspace,
+                          void* stream);
 fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
                                      const float* scale, uint8_t* q, uint8_t* qT,
-                                     float* amax_out, void* stream);
+                                     float* amax_out, void* workspace, void* stream);
 
 /* One delayed-scaling step.  [guide] delayed scaling keeps a buffer of the
  * maxima of past steps; [colossal] delayed scaling takes the scale from a
@@ -297,14 +324,15 @@ fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, i
  *   y_bf16  out [M][N] BF16, may be NULL when y_q is given
  *   y_fmt   FP8 format of y_q;  y_scale  in float[1]
  *   y_q     out uint8 [M][N];   y_amax   out float[1]
+ *   workspace  see Workspace; needed with y_amax, else may be NULL
  * At least one of y_q / y_amax must be given (else FP8_ERR_NULL; the plain
  * call is fp8_gemm_fprop).  N % 16 == 0 (FP8_ERR_ALIGN); at most 65536
- * 256x256 output tiles (FP8_ERR_SHAPE).  y_amax uses the workspace described
- * under Memory.  Other rules and errors as fp8_gemm_fprop. */
+ * 256x256 output tiles (FP8_ERR_SHAPE).  Other rules and errors as
+ * fp8_gemm_fprop. */
 fp8_status_t fp8_gemm_fprop_fused(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,
                                   int64_t N, int64_t K, void* y_bf16, int32_t y_fmt,
                                   const float* y_scale, uint8_t* y_q, float* y_amax,
-                                  void* stream);
+                                  void* workspace, void* stream);
 
 /* wgrad with an FP32 result, optionally accumulated.  [snippets] forward-
  * pass snippet: the master weights are FP32, so their gradient is too;

@@ -2,8 +2,9 @@
 // in include/fp8sg.h).  Each call checks its arguments on the host, in the
 // order NULL -> enum -> shape -> alignment (a NULL data pointer is accepted
 // for an empty tensor, so the NULL check of data follows the shape check),
-// and only then enqueues kernels on the caller's stream.  Nothing here
-// allocates or synchronises.
+// and only then enqueues kernels on the caller's stream.  Nothing here or
+// in the launchers allocates, synchronises or keeps state between calls:
+// the amax-producing calls reduce through the caller's workspace.
 #include "fp8sg.h"
 
 #include <stdint.h>
@@ -31,6 +32,11 @@ bool have(const void* p, int64_t elems) { return p != nullptr || elems == 0; }
 
 bool is_block(int32_t sc) { return sc == FP8_SCALE_BLOCK_1x128 || sc == FP8_SCALE_BLOCK_128x128; }
 
+// The caller's workspace: FP8_WORKSPACE_BYTES of device memory, 256-byte
+// aligned (the grid-wide maximum's words sit in whole 128-byte lines).
+static_assert(FP8_WORKSPACE_BYTES == fp8sg::kWorkspaceTotalWords * 4, "workspace size");
+uint32_t* wsp(void* ws) { return static_cast<uint32_t*>(ws); }
+
 // C[rows_a][rows_b] = A[rows_a][kc] . B[rows_b][kc]^T with the operands' scales.
 // Optional fused epilogue of the BF16 mode: the next layer's FP8 copy of the
 // output (with its scale and format) and the output's amax.
@@ -39,6 +45,7 @@ struct Fused {
   const float* q_scale = nullptr;
   int q_fmt = 0;
   float* amax = nullptr;
+  void* ws = nullptr;       // the caller's workspace (with amax)
 };
 
 fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a,
@@ -67,7 +74,8 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   // FP8 copy is written instead
   const bool c_ok = have(c, nc) || fu.cq != nullptr;
   if (!have(a->data, rows_a * kc) || !have(b->data, rows_b * kc) || !c_ok ||
-      !have(a->scale_inv, nc) || !have(b->scale_inv, nc) || (fu.cq && !fu.q_scale))
+      !have(a->scale_inv, nc) || !have(b->scale_inv, nc) || (fu.cq && !fu.q_scale) ||
+      (fu.amax && !fu.ws))
     return FP8_ERR_NULL;
   if (mode == 1) {
     if (kc % 128) return FP8_ERR_SHAPE;
@@ -80,7 +88,7 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   if (kc % 16) return FP8_ERR_ALIGN;
   if (!aligned(a->data, 16) || !aligned(b->data, 16) || !aligned(c, 16)) return FP8_ERR_ALIGN;
   if (fused && (rows_b % 16 || !aligned(fu.cq, 16) || !aligned(fu.q_scale, 4) ||
-                !aligned(fu.amax, 4)))
+                !aligned(fu.amax, 4) || !aligned(fu.ws, 256)))
     return FP8_ERR_ALIGN;
   if (mode != 2 && (!aligned(a->scale_inv, 4) || !aligned(b->scale_inv, 4)))
     return FP8_ERR_ALIGN;
@@ -95,6 +103,7 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
   p.q_scale = fu.q_scale;
   p.q_fmt = fu.q_fmt;
   p.amax = fu.amax;
+  p.ws = wsp(fu.ws);
   p.part = nullptr;
   p.M = rows_a;
   p.N = rows_b;
@@ -109,20 +118,22 @@ fp8_status_t gemm(const fp8_operand_t* a, const fp8_operand_t* b, int64_t rows_a
 
 // amax / per-tensor cast of BF16 (in = 0) or FP32 (in = 1) input.
 fp8_status_t amax_any(const void* x, int64_t rows, int64_t cols, int32_t fmt, float* amax,
-                      float* scale, float* scale_inv, void* stream, int in) {
-  if (!amax) return FP8_ERR_NULL;
+                      float* scale, float* scale_inv, void* ws, void* stream, int in) {
+  if (!amax || !ws) return FP8_ERR_NULL;
   if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
   if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
   if (!have(x, rows * cols)) return FP8_ERR_NULL;
   if (!aligned(x, 16) || !aligned(amax, 4) || (scale && !aligned(scale, 4)) ||
-      (scale_inv && !aligned(scale_inv, 4)))
+      (scale_inv && !aligned(scale_inv, 4)) || !aligned(ws, 256))
     return FP8_ERR_ALIGN;
-  return hip(fp8sg::launch_amax(x, rows * cols, fmt, amax, scale, scale_inv, st(stream), in));
+  return hip(fp8sg::launch_amax(x, rows * cols, fmt, amax, scale, scale_inv, wsp(ws), st(stream),
+                                in));
 }
 
 fp8_status_t quantize_tensor_any(const void* x, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                 void* stream, int in) {
+                                 void* ws, void* stream, int in) {
+  if (amax_out && !ws) return FP8_ERR_NULL;
   if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
   if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
   if (!have(x, rows * cols) || !have(q, rows * cols) || !have(scale, rows * cols))
@@ -130,46 +141,57 @@ fp8_status_t quantize_tensor_any(const void* x, int64_t rows, int64_t cols, int3
   if (cols % 16) return FP8_ERR_ALIGN;
   if (qT && rows % 16) return FP8_ERR_ALIGN;
   if (!aligned(x, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) || !aligned(scale, 4) ||
-      (amax_out && !aligned(amax_out, 4)))
+      (amax_out && (!aligned(amax_out, 4) || !aligned(ws, 256))))
     return FP8_ERR_ALIGN;
   return hip(fp8sg::launch_quantize_tensor(x, rows, cols, fmt, scale, q, qT, amax_out,
-                                           st(stream), in));
+                                           amax_out ? wsp(ws) : nullptr, st(stream), in));
 }
 
 }  // namespace
 
 extern "C" {
 
+fp8_status_t fp8_workspace_init(void* workspace, int32_t wait_polls, void* stream) {
+  if (!workspace) return FP8_ERR_NULL;
+  if (wait_polls < 0) return FP8_ERR_SHAPE;
+  if (!aligned(workspace, 256)) return FP8_ERR_ALIGN;
+  return hip(fp8sg::launch_workspace_init(wsp(workspace), (uint32_t)wait_polls, st(stream)));
+}
+
 fp8_status_t fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt, float* amax,
-                      float* scale, float* scale_inv, void* stream) {
-  return amax_any(x_bf16, rows, cols, fmt, amax, scale, scale_inv, stream, 0);
+                      float* scale, float* scale_inv, void* workspace, void* stream) {
+  return amax_any(x_bf16, rows, cols, fmt, amax, scale, scale_inv, workspace, stream, 0);
 }
 
 fp8_status_t fp8_amax_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
-                          float* amax, float* scale, float* scale_inv, void* stream) {
-  return amax_any(x_f32, rows, cols, fmt, amax, scale, scale_inv, stream, 1);
+                          float* amax, float* scale, float* scale_inv, void* workspace,
+                          void* stream) {
+  return amax_any(x_f32, rows, cols, fmt, amax, scale, scale_inv, workspace, stream, 1);
 }
 
 fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols, int32_t fmt,
                                  const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                 void* stream) {
-  return quantize_tensor_any(x_bf16, rows, cols, fmt, scale, q, qT, amax_out, stream, 0);
+                                 void* workspace, void* stream) {
+  return quantize_tensor_any(x_bf16, rows, cols, fmt, scale, q, qT, amax_out, workspace, stream,
+                             0);
 }
 
 fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64_t cols,
                                          int32_t fmt, uint8_t* q, uint8_t* qT, float* amax,
-                                         float* scale, float* scale_inv, void* stream) {
-  if (!amax || !scale_inv) return FP8_ERR_NULL;
+                                         float* scale, float* scale_inv, void* workspace,
+                                         void* stream) {
+  if (!amax || !scale_inv || !workspace) return FP8_ERR_NULL;
   if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
   if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
   if (!have(x_bf16, rows * cols) || !have(q, rows * cols)) return FP8_ERR_NULL;
   if (cols % 16) return FP8_ERR_ALIGN;
   if (qT && rows % 16) return FP8_ERR_ALIGN;
   if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||
-      !aligned(amax, 4) || !aligned(scale_inv, 4) || (scale && !aligned(scale, 4)))
+      !aligned(amax, 4) || !aligned(scale_inv, 4) || (scale && !aligned(scale, 4)) ||
+      !aligned(workspace, 256))
     return FP8_ERR_ALIGN;
   return hip(fp8sg::launch_quantize_current(x_bf16, rows, cols, fmt, q, qT, amax, scale,
-                                            scale_inv, st(stream), 0));
+                                            scale_inv, wsp(workspace), st(stream), 0));
 }
 
 static fp8_status_t current_ok(const void* x, int64_t rows, int64_t cols, int32_t fmt,
@@ -191,20 +213,22 @@ fp8_status_t fp8_quantize_pair_current(const void* a_bf16, int64_t a_rows, int64
                                        float* a_scale, float* a_scale_inv, const void* b_bf16,
                                        int64_t b_rows, int64_t b_cols, int32_t b_fmt,
                                        uint8_t* b_q, float* b_amax, float* b_scale,
-                                       float* b_scale_inv, void* stream) {
+                                       float* b_scale_inv, void* workspace, void* stream) {
+  if (!workspace) return FP8_ERR_NULL;
   fp8_status_t e = current_ok(a_bf16, a_rows, a_cols, a_fmt, a_q, a_amax, a_scale, a_scale_inv);
   if (e != FP8_OK) return e;
   e = current_ok(b_bf16, b_rows, b_cols, b_fmt, b_q, b_amax, b_scale, b_scale_inv);
   if (e != FP8_OK) return e;
+  if (!aligned(workspace, 256)) return FP8_ERR_ALIGN;
   const fp8sg::CurrentTensor ta{a_bf16, a_rows, a_cols, a_fmt, a_q, a_amax, a_scale, a_scale_inv};
   const fp8sg::CurrentTensor tb{b_bf16, b_rows, b_cols, b_fmt, b_q, b_amax, b_scale, b_scale_inv};
-  return hip(fp8sg::launch_quantize_pair_current(ta, tb, st(stream)));
+  return hip(fp8sg::launch_quantize_pair_current(ta, tb, wsp(workspace), st(stream)));
 }
 
 fp8_status_t fp8_quantize_tensor_f32(const float* x_f32, int64_t rows, int64_t cols, int32_t fmt,
                                      const float* scale, uint8_t* q, uint8_t* qT,
-                                     float* amax_out, void* stream) {
-  return quantize_tensor_any(x_f32, rows, cols, fmt, scale, q, qT, amax_out, stream, 1);
+                                     float* amax_out, void* workspace, void* stream) {
+  return quantize_tensor_any(x_f32, rows, cols, fmt, scale, q, qT, amax_out, workspace, stream, 1);
 }
 
 fp8_status_t fp8_amax_history_update(float* history, int32_t history_len, int64_t step,
@@ -293,12 +317,13 @@ fp8_status_t fp8_gemm_wgrad(const fp8_operand_t* dyT, const fp8_operand_t* xT, i
 fp8_status_t fp8_gemm_fprop_fused(const fp8_operand_t* x, const fp8_operand_t* w, int64_t M,
                                   int64_t N, int64_t K, void* y_bf16, int32_t y_fmt,
                                   const float* y_scale, uint8_t* y_q, float* y_amax,
-                                  void* stream) {
+                                  void* workspace, void* stream) {
   Fused fu;
   fu.cq = y_q;
   fu.q_scale = y_scale;
   fu.q_fmt = y_fmt;
   fu.amax = y_amax;
+  fu.ws = workspace;
   if (!y_q && !y_amax) return FP8_ERR_NULL;   // use fp8_gemm_fprop
   return gemm(x, w, M, N, K, y_bf16, stream, 0, fu);
 }

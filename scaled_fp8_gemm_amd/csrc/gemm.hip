@@ -298,11 +298,7 @@ hipError_t launch_gemm(const GemmProblem& q0, hipStream_t s) {
     return hipSuccess;
   }
   GemmProblem q = q0;
-  q.part = nullptr;
-  if (q.amax) {
-    hipError_t err = stream_partials(s, &q.part);
-    if (err != hipSuccess) return err;
-  }
+  q.part = q.amax ? q.ws : nullptr;   // per-tile maxima in the caller's workspace
   hipError_t err;
   if (q.mode == kTensor)
     err = w8::run_fmt<kTensor, 1, 1>(q, s);

@@ -9,28 +9,40 @@ namespace fp8sg {
 
 int device_cu_count();
 
-// Per-(device, stream) buffer of kWorkspaceWords partial maxima (FP32
-// magnitude bits), allocated on first use.
+// The caller's workspace (FP8_WORKSPACE_BYTES, 256-byte aligned), in words:
+//   [0, kWorkspaceWords)            partial maxima (FP32 magnitude bits): at
+//                                   most kMaxPartials per quantise launch, one
+//                                   per output tile for the GEMM's fused amax
+//   [kGridWordsAt, +kGridMaxWords)  grid-wide maxima of the one-launch current
+//                                   scaling (two sets, one per tensor of the
+//                                   paired launch; counters, maxima and flags,
+//                                   one 128-byte line each); zero before first
+//                                   use, and left zero by every launch
+//   [kConfigAt, +kConfigWords)      word 0: bound on the polls of the
+//                                   grid-wide wait (0 = the default)
 constexpr int kWorkspaceWords = 1 << 16;
-// followed by kGridMaxWords words for the grid-wide maxima of the one-launch
-// current scaling (two sets, one per tensor of the paired launch; counters,
-// maxima and flags, one 128-byte line each; zero when allocated)
 constexpr int kGridMaxWords = 260 * 32;
-hipError_t stream_partials(hipStream_t s, uint32_t** out);
+constexpr int kConfigWords = 32;
+constexpr int kGridWordsAt = kWorkspaceWords;
+constexpr int kConfigAt = kWorkspaceWords + kGridMaxWords;
+constexpr int kWorkspaceTotalWords = kConfigAt + kConfigWords;
+// Clear a workspace for first use and set its wait bound (a fill kernel).
+hipError_t launch_workspace_init(uint32_t* ws, uint32_t wait_polls, hipStream_t s);
 // amax[0] = the largest of part[0 .. n-1], as an FP32 value.
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s);
 
 // in: 0 = BF16 input, 1 = FP32 input
+// ws: the caller's workspace (may be NULL where no amax is produced)
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
-                       float* scale_inv, hipStream_t s, int in);
+                       float* scale_inv, uint32_t* ws, hipStream_t s, int in);
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                  hipStream_t s, int in);
+                                  uint32_t* ws, hipStream_t s, int in);
 // amax -> scale pair -> cast (current scaling): one launch when the tensor fits
 // a grid the device holds at once, else two.
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
-                                   float* scale_inv, hipStream_t s, int in);
+                                   float* scale_inv, uint32_t* ws, hipStream_t s, int in);
 // One BF16 tensor under current scaling, without a transposed copy.
 struct CurrentTensor {
   const void* x;
@@ -44,7 +56,7 @@ struct CurrentTensor {
 // Current scaling of two tensors in one launch when the device holds both
 // at once, else one launch_quantize_current each.
 hipError_t launch_quantize_pair_current(const CurrentTensor& a, const CurrentTensor& b,
-                                        hipStream_t s);
+                                        uint32_t* ws, hipStream_t s);
 hipError_t launch_history_update(float* hist, int hlen, int64_t step, const float* amax, int fmt,
                                  float* scale, float* scale_inv, hipStream_t s);
 hipError_t launch_quantize_block(const void* x, int64_t rows, int64_t cols, int fmt, int br,
@@ -75,6 +87,7 @@ struct GemmProblem {
   const float* q_scale; // its scale (device float[1])
   int q_fmt;            // its format
   float* amax;          // amax of the BF16-rounded output, or NULL
+  uint32_t* ws;         // the caller's workspace (needed with amax)
   uint32_t* part;       // set by launch_gemm: per-tile maxima for amax
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);

@@ -9,13 +9,11 @@
 // FP8 copy (1 B); they use 16-byte vector loads, grid-stride loops sized to
 // the CU count, and reduce maxima as unsigned magnitude bits (exact and
 // order-independent).  A kernel that produces an amax writes one partial
-// maximum per workgroup into a small per-stream workspace and a one-block
-// finalize kernel reduces them; same-address device atomics from thousands of
+// maximum per workgroup into the caller's workspace and a one-block finalize
+// kernel reduces them; same-address device atomics from thousands of
 // workgroups serialise (about 10 ns each on MI355X) and would cost more than
 // the pass itself.
 #include <atomic>
-#include <mutex>
-#include <vector>
 
 #include "fp8_device.h"
 #include "launch.h"
@@ -238,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x
 //
 // The grid-wide maximum uses device-coherent atomics only (agent-scope
 // fences would write back and invalidate whole L2s, which costs more than
-// the pass it saves).  Its words live in the per-stream workspace after the
-// partials, zero when allocated, each in a cache line of its own (kLine
+// the pass it saves).  Its words live in the caller's workspace after the
+// partials, zero before first use, each in a cache line of its own (kLine
 // words).  Workgroups form groups of kGroup:
 //   * a workgroup reads its group's flag (a generation number and a value),
 //     atomically maxes its maximum into the group's word, then (once that
@@ -256,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x
 // most kGroup + kMaxGroups long.
 // The wait is bounded: a grid that is not all resident (other work holding
 // CUs, such as a second such launch on another stream) could otherwise wait
-// for ever.  A workgroup whose wait runs out (kSpinLimit polls, about 7 ms measured)
-// reduces the whole input itself, so the result is the same, only slower.
-constexpr int kSpinLimit = 1 << 15;
+// for ever.  A workgroup whose wait runs out reduces the whole input itself,
+// so the result is the same, only slower.  The bound is the workspace's
+// config word, or kSpinLimit polls (about 7 ms measured) when that is 0.
+constexpr uint32_t kSpinLimit = 1u << 15;
 constexpr int kLine = 32;                             // words per 128-byte line
 constexpr int kGroup = 32;                            // workgroups per group
 constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
@@ -291,9 +290,10 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
 
 // The largest m over the nblocks workgroups that share the words at w, in
 // every one of them (kNoMax if the wait ran out); `block` is the calling
-// workgroup's index among them.  All threads call it; thread 0 does the work.
-__device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t block,
-                                             uint32_t nblocks, uint32_t* sh) {
+// workgroup's index among them; cfg[0] bounds the polls (0: kSpinLimit).
+// All threads call it; thread 0 does the work.
+__device__ __forceinline__ uint32_t grid_max(uint32_t* w, const uint32_t* cfg, uint32_t m,
+                                             uint32_t block, uint32_t nblocks, uint32_t* sh) {
   if (threadIdx.x == 0) {
     const int g = (int)(block / kGroup);
     const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
@@ -322,7 +322,9 @@ __device__ __forceinline__ uint32_t grid_max(uint32_t* w, uint32_t m, uint32_t b
       for (int i = 0; i < kMaxGroups; ++i)
         __hip_atomic_store(gm_flag(w, i), f1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      for (int spin = 0; spin < kSpinLimit; ++spin) {
+      const uint32_t c = *cfg;
+      const uint32_t limit = c != 0 ? c : kSpinLimit;
+      for (uint32_t spin = 0; spin < limit; ++spin) {
         const uint64_t f =
             __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((uint32_t)(f >> 32) != gen) {
@@ -344,6 +346,7 @@ struct PairTensor {
   int64_t nvec;
   uint2* q;             // FP8 output, 8 bytes per vector
   uint32_t* gw;         // its grid-wide maximum words
+  const uint32_t* cfg;  // the workspace's config word (wait bound)
   float* amax;
   float* scale;
   float* scale_inv;
@@ -400,7 +403,7 @@ __device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
     for (int l = 0; l < L; ++l) m = max(m, absmax8(lv[l][t]));
   }
   m = block_max_u32<kThreads>(m << 16, red);
-  uint32_t a = grid_max(T.gw, m, b, T.nblocks, sh);
+  uint32_t a = grid_max(T.gw, T.cfg, m, b, T.nblocks, sh);
   if (a == kNoMax) {
     a = 0;
     for (int64_t i = t; i < T.nvec; i += kThreads) a = max(a, absmax8(T.x[i]) << 16);
@@ -450,10 +453,11 @@ template <int FMT, int U>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
     const uint4* __restrict__ x, int64_t nvec, uint2* __restrict__ q, uint32_t* __restrict__ gw,
-    float* __restrict__ amax, float* __restrict__ scale, float* __restrict__ scale_inv) {
+    const uint32_t* __restrict__ cfg, float* __restrict__ amax, float* __restrict__ scale,
+    float* __restrict__ scale_inv) {
   __shared__ uint32_t red[kThreads / 64];
   __shared__ uint32_t sh;
-  const PairTensor T{x, nvec, q, gw, amax, scale, scale_inv, gridDim.x};
+  const PairTensor T{x, nvec, q, gw, cfg, amax, scale, scale_inv, gridDim.x};
   amax_cast_held<FMT, U, 0>(T, blockIdx.x, nullptr, red, &sh);
 }
 
@@ -1066,44 +1070,19 @@ int grid_for(int64_t work_items, int per_block) {
 
 }  // namespace
 
-// One partial-maximum buffer (kWorkspaceWords words: a quantise launch uses
-// at most kMaxPartials, a GEMM with a fused amax one per output tile), then
-// kGridMaxWords for the one-launch current scaling's grid-wide maximum, per
-// (device, stream), allocated (and those words cleared) on first use
-// and kept until the process ends.
-// Work on one stream runs in order, so successive calls on a stream share its
-// buffer safely; calls on different streams never share one.
-struct StreamBuffer {
-  int dev;
-  hipStream_t stream;
-  uint32_t* p;
-};
-static std::mutex g_partials_mu;
-static std::vector<StreamBuffer> g_partials;
+// Workspace set-up: every word zero except the config word, which holds the
+// grid-wide wait's poll bound.  A fill kernel rather than a memset, so the
+// call may be captured in a graph.
+__global__ __launch_bounds__(kThreads) void k_workspace_init(uint32_t* __restrict__ ws,
+                                                             uint32_t wait_polls) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < kWorkspaceTotalWords;
+       i += gridDim.x * kThreads)
+    ws[i] = i == kConfigAt ? wait_polls : 0u;
+}
 
-hipError_t stream_partials(hipStream_t s, uint32_t** out) {
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  std::lock_guard<std::mutex> lock(g_partials_mu);
-  for (const StreamBuffer& b : g_partials)
-    if (b.dev == dev && b.stream == s) {
-      *out = b.p;
-      return hipSuccess;
-    }
-  void* p = nullptr;
-  err = hipMalloc(&p, (kWorkspaceWords + kGridMaxWords) * sizeof(uint32_t));
-  if (err != hipSuccess) return err;
-  // the grid-wide maximum's words start at zero
-  err = hipMemsetAsync(static_cast<uint32_t*>(p) + kWorkspaceWords, 0,
-                       kGridMaxWords * sizeof(uint32_t), s);
-  if (err != hipSuccess) {
-    (void)hipFree(p);
-    return err;
-  }
-  g_partials.push_back({dev, s, static_cast<uint32_t*>(p)});
-  *out = static_cast<uint32_t*>(p);
-  return hipSuccess;
+hipError_t launch_workspace_init(uint32_t* ws, uint32_t wait_polls, hipStream_t s) {
+  hipLaunchKernelGGL(k_workspace_init, dim3(64), dim3(kThreads), 0, s, ws, wait_polls);
+  return hipGetLastError();
 }
 
 int device_cu_count() {
@@ -1132,10 +1111,8 @@ int device_cu_count() {
   } while (0)
 
 hipError_t launch_amax(const void* x, int64_t n, int fmt, float* amax, float* scale,
-                       float* scale_inv, hipStream_t s, int in) {
-  uint32_t* part = nullptr;
-  hipError_t err = stream_partials(s, &part);
-  if (err != hipSuccess) return err;
+                       float* scale_inv, uint32_t* ws, hipStream_t s, int in) {
+  uint32_t* part = ws;
   const int per = in == kInBF16 ? 8 : 4;   // elements per 16-byte vector
   const int64_t nvec = n / per;
   const int ntail = (int)(n - nvec * per);
@@ -1211,12 +1188,8 @@ static void cast_kernels(const void* x, int64_t rows, int64_t cols, int fmt, Sca
 
 hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int fmt,
                                   const float* scale, uint8_t* q, uint8_t* qT, float* amax_out,
-                                  hipStream_t s, int in) {
-  uint32_t* part = nullptr;
-  if (amax_out) {
-    hipError_t err = stream_partials(s, &part);
-    if (err != hipSuccess) return err;
-  }
+                                  uint32_t* ws, hipStream_t s, int in) {
+  uint32_t* part = amax_out ? ws : nullptr;
   ScaleSrc src{scale, nullptr, 0, nullptr, nullptr, nullptr};
   int g = 0;
   if (rows * cols > 0) {
@@ -1257,7 +1230,7 @@ static int coop_capacity() {
 // far more than the pass it saves; the grid maximum's bounded wait covers
 // the rare grid that is not all resident.)
 template <int FMT, int U>
-static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_t* part,
+static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_t* ws,
                                 float* amax, float* scale, float* scale_inv, hipStream_t s,
                                 bool* done) {
   const int64_t g = (nvec + (int64_t)U * kThreads - 1) / ((int64_t)U * kThreads);
@@ -1265,9 +1238,8 @@ static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_
   if (g > cap || g > kMaxPartials) return hipSuccess;
   const uint4* xv = static_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(q);
-  uint32_t* gw = part + kWorkspaceWords;
   hipLaunchKernelGGL((k_amax_cast<FMT, U>), dim3((unsigned)g), dim3(kThreads), 0, s, xv, nvec,
-                     qv, gw, amax, scale, scale_inv);
+                     qv, ws + kGridWordsAt, ws + kConfigAt, amax, scale, scale_inv);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) *done = true;
   return err;
@@ -1275,12 +1247,11 @@ static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_
 
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
-                                   float* scale_inv, hipStream_t s, int in) {
+                                   float* scale_inv, uint32_t* ws, hipStream_t s, int in) {
   const int64_t n = rows * cols;
-  if (n == 0) return launch_amax(x, 0, fmt, amax, scale, scale_inv, s, in);
-  uint32_t* part = nullptr;
-  hipError_t err = stream_partials(s, &part);
-  if (err != hipSuccess) return err;
+  if (n == 0) return launch_amax(x, 0, fmt, amax, scale, scale_inv, ws, s, in);
+  uint32_t* part = ws;
+  hipError_t err = hipSuccess;
   // One launch when the tensor fits the registers of a co-resident grid:
   // BF16, whole 16-byte vectors, no transposed copy.
   if (in == kInBF16 && qT == nullptr && n % 8 == 0) {
@@ -1288,9 +1259,9 @@ hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, in
     FP8SG_FMT_DISPATCH(fmt, {
       // 16 vectors per thread (fewer workgroups, a shorter arrival chain; on
       // MI355X up to ~50M elements), then 24
-      err = try_amax_cast<F, 16>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+      err = try_amax_cast<F, 16>(x, n / 8, q, ws, amax, scale, scale_inv, s, &done);
       if (err == hipSuccess && !done)
-        err = try_amax_cast<F, 24>(x, n / 8, q, part, amax, scale, scale_inv, s, &done);
+        err = try_amax_cast<F, 24>(x, n / 8, q, ws, amax, scale, scale_inv, s, &done);
     });
     if (err != hipSuccess) return err;
     if (done) return hipSuccess;
@@ -1352,19 +1323,18 @@ static hipError_t try_pair(PairArgs& a, hipStream_t s, bool* done) {
 }
 
 hipError_t launch_quantize_pair_current(const CurrentTensor& ta, const CurrentTensor& tb,
-                                        hipStream_t s) {
+                                        uint32_t* ws, hipStream_t s) {
   const int64_t na = ta.rows * ta.cols, nb = tb.rows * tb.cols;
   if (na > 0 && nb > 0) {
-    uint32_t* part = nullptr;
-    hipError_t err = stream_partials(s, &part);
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
     PairArgs a;
     const CurrentTensor* in[2] = {&ta, &tb};
     for (int i = 0; i < 2; ++i) {
       a.t[i].x = static_cast<const uint4*>(in[i]->x);
       a.t[i].nvec = in[i]->rows * in[i]->cols / 8;
       a.t[i].q = reinterpret_cast<uint2*>(in[i]->q);
-      a.t[i].gw = part + kWorkspaceWords + i * kGridSetWords;
+      a.t[i].gw = ws + kGridWordsAt + i * kGridSetWords;
+      a.t[i].cfg = ws + kConfigAt;
       a.t[i].amax = in[i]->amax;
       a.t[i].scale = in[i]->scale;
       a.t[i].scale_inv = in[i]->scale_inv;
@@ -1383,10 +1353,10 @@ hipError_t launch_quantize_pair_current(const CurrentTensor& ta, const CurrentTe
   }
   // an empty tensor, or a pair the device cannot hold at once: one call each
   hipError_t err = launch_quantize_current(ta.x, ta.rows, ta.cols, ta.fmt, ta.q, nullptr, ta.amax,
-                                           ta.scale, ta.scale_inv, s, kInBF16);
+                                           ta.scale, ta.scale_inv, ws, s, kInBF16);
   if (err != hipSuccess) return err;
   return launch_quantize_current(tb.x, tb.rows, tb.cols, tb.fmt, tb.q, nullptr, tb.amax, tb.scale,
-                                 tb.scale_inv, s, kInBF16);
+                                 tb.scale_inv, ws, s, kInBF16);
 }
 
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s) {

@@ -24,8 +24,12 @@ int main(void) {
   fp8_operand_t a = {q, FP8_E4M3, FP8_SCALE_TENSOR, p};
   fp8_operand_t b = {q, FP8_E4M3, FP8_SCALE_BLOCK_1x128, p};
 
-  expect("amax NULL x", fp8_amax(NULL, 4, 16, FP8_E4M3, f, NULL, NULL, NULL), FP8_ERR_NULL);
-  expect("cast cols % 16", fp8_quantize_tensor(p, 4, 24, FP8_E4M3, f, q, NULL, NULL, NULL),
+  expect("amax NULL x", fp8_amax(NULL, 4, 16, FP8_E4M3, f, NULL, NULL, p, NULL), FP8_ERR_NULL);
+  expect("amax NULL workspace", fp8_amax(p, 4, 16, FP8_E4M3, f, NULL, NULL, NULL, NULL),
+         FP8_ERR_NULL);
+  expect("workspace init misaligned", fp8_workspace_init((char*)p + 128, 0, NULL),
+         FP8_ERR_ALIGN);
+  expect("cast cols % 16", fp8_quantize_tensor(p, 4, 24, FP8_E4M3, f, q, NULL, NULL, NULL, NULL),
          FP8_ERR_ALIGN);
   expect("block 1x96", fp8_quantize_block(p, 4, 128, FP8_E4M3, 1, 96, q, f, NULL),
          FP8_ERR_UNSUPPORTED);
@@ -39,7 +43,7 @@ int main(void) {
          FP8_ERR_UNSUPPORTED);
   expect("pair NULL b amax",
          fp8_quantize_pair_current(p, 4, 16, FP8_E4M3, q, f, NULL, f, p, 4, 16, FP8_E4M3, q, NULL,
-                                   NULL, f, NULL),
+                                   NULL, f, p, NULL),
          FP8_ERR_NULL);
   if (strncmp(fp8_status_string(FP8_OK), "FP8_OK", 6) != 0) ++failures;
   return failures != 0;

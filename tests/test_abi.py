@@ -41,24 +41,38 @@ def test_status_strings(L):
 
 
 def test_amax_errors(L):
-    assert L.fp8_amax(None, 4, 16, 0, P, None, None, None) == NULL
-    assert L.fp8_amax(P, 4, 16, 0, None, None, None, None) == NULL
-    assert L.fp8_amax(P, 4, 16, 7, P, None, None, None) == UNSUP
-    assert L.fp8_amax(P, -1, 16, 0, P, None, None, None) == SHAPE
-    assert L.fp8_amax(PU, 4, 16, 0, P, None, None, None) == ALIGN
-    assert L.fp8_amax(P, 4, 16, 0, P + 2, None, None, None) == ALIGN
+    assert L.fp8_amax(None, 4, 16, 0, P, None, None, P, None) == NULL
+    assert L.fp8_amax(P, 4, 16, 0, None, None, None, P, None) == NULL
+    assert L.fp8_amax(P, 4, 16, 0, P, None, None, None, None) == NULL     # workspace
+    assert L.fp8_amax(P, 4, 16, 7, P, None, None, P, None) == UNSUP
+    assert L.fp8_amax(P, -1, 16, 0, P, None, None, P, None) == SHAPE
+    assert L.fp8_amax(PU, 4, 16, 0, P, None, None, P, None) == ALIGN
+    assert L.fp8_amax(P, 4, 16, 0, P + 2, None, None, P, None) == ALIGN
+    assert L.fp8_amax(P, 4, 16, 0, P, None, None, P + 128, None) == ALIGN  # workspace % 256
+
+
+def test_workspace_init_errors(L):
+    from scaled_fp8_gemm_amd import fp8sg
+    assert fp8sg.WORKSPACE_BYTES == int(re.search(r"#define FP8_WORKSPACE_BYTES (\d+)",
+                                                  open(HEADER).read()).group(1))
+    w = L.fp8_workspace_init
+    assert w(None, 0, None) == NULL
+    assert w(P, -1, None) == SHAPE
+    assert w(P + 16, 0, None) == ALIGN
 
 
 def test_quantize_tensor_errors(L):
     q = L.fp8_quantize_tensor
-    assert q(None, 4, 16, 0, P, P, None, None, None) == NULL
-    assert q(P, 4, 16, 0, None, P, None, None, None) == NULL
-    assert q(P, 4, 16, 0, P, None, None, None, None) == NULL
-    assert q(P, 4, 16, 2, P, P, None, None, None) == UNSUP
-    assert q(P, 4, -16, 0, P, P, None, None, None) == SHAPE
-    assert q(P, 4, 24, 0, P, P, None, None, None) == ALIGN          # cols % 16
-    assert q(P, 8, 16, 0, P, P, P, None, None) == ALIGN             # qT needs rows % 16
-    assert q(PU, 16, 16, 0, P, P, None, None, None) == ALIGN
+    assert q(None, 4, 16, 0, P, P, None, None, None, None) == NULL
+    assert q(P, 4, 16, 0, None, P, None, None, None, None) == NULL
+    assert q(P, 4, 16, 0, P, None, None, None, None, None) == NULL
+    assert q(P, 4, 16, 2, P, P, None, None, None, None) == UNSUP
+    assert q(P, 4, -16, 0, P, P, None, None, None, None) == SHAPE
+    assert q(P, 4, 24, 0, P, P, None, None, None, None) == ALIGN          # cols % 16
+    assert q(P, 8, 16, 0, P, P, P, None, None, None) == ALIGN             # qT needs rows % 16
+    assert q(PU, 16, 16, 0, P, P, None, None, None, None) == ALIGN
+    assert q(P, 16, 16, 0, P, P, None, P, None, None) == NULL       # amax_out needs a workspace
+    assert q(P, 16, 16, 0, P, P, None, P, P + 64, None) == ALIGN
 
 
 def test_history_errors(L):
@@ -86,40 +100,45 @@ def test_block_and_mx_errors(L):
 
 def test_quantize_current_errors(L):
     c = L.fp8_quantize_tensor_current
-    assert c(P, 4, 16, 0, P, None, None, None, P, None) == NULL        # amax
-    assert c(P, 4, 16, 0, P, None, P, None, None, None) == NULL        # scale_inv
-    assert c(P, 4, 24, 0, P, None, P, None, P, None) == ALIGN          # cols % 16
-    assert c(P, 8, 16, 0, P, P, P, None, P, None) == ALIGN             # qT rows % 16
-    assert c(P, 4, 16, 2, P, None, P, None, P, None) == UNSUP
+    assert c(P, 4, 16, 0, P, None, None, None, P, P, None) == NULL     # amax
+    assert c(P, 4, 16, 0, P, None, P, None, None, P, None) == NULL     # scale_inv
+    assert c(P, 4, 16, 0, P, None, P, None, P, None, None) == NULL     # workspace
+    assert c(P, 4, 24, 0, P, None, P, None, P, P, None) == ALIGN       # cols % 16
+    assert c(P, 8, 16, 0, P, P, P, None, P, P, None) == ALIGN          # qT rows % 16
+    assert c(P, 4, 16, 0, P, None, P, None, P, P + 16, None) == ALIGN  # workspace % 256
+    assert c(P, 4, 16, 2, P, None, P, None, P, P, None) == UNSUP
 
 
 def test_quantize_pair_current_errors(L):
     c = L.fp8_quantize_pair_current
     good = (P, 4, 16, 0, P, P, None, P)
-    assert c(P, 4, 16, 0, P, None, None, P, *good, None) == NULL        # a's amax
-    assert c(*good, P, 4, 16, 0, P, P, None, None, None) == NULL        # b's scale_inv
-    assert c(None, 4, 16, 0, P, P, None, P, *good, None) == NULL        # a's input
-    assert c(*good, P, 4, 16, 0, None, P, None, P, None) == NULL        # b's output
-    assert c(P, -1, 16, 0, P, P, None, P, *good, None) == SHAPE
-    assert c(*good, P, 4, 24, 0, P, P, None, P, None) == ALIGN          # b's cols % 16
-    assert c(PU, 4, 16, 0, P, P, None, P, *good, None) == ALIGN
-    assert c(*good, P, 4, 16, 0, P, P, PU, P, None) == ALIGN            # b's scale
-    assert c(P, 4, 16, 2, P, P, None, P, *good, None) == UNSUP
-    assert c(*good, P, 4, 16, 5, P, P, None, P, None) == UNSUP
+    assert c(P, 4, 16, 0, P, None, None, P, *good, P, None) == NULL        # a's amax
+    assert c(*good, P, 4, 16, 0, P, P, None, None, P, None) == NULL        # b's scale_inv
+    assert c(None, 4, 16, 0, P, P, None, P, *good, P, None) == NULL        # a's input
+    assert c(*good, P, 4, 16, 0, None, P, None, P, P, None) == NULL        # b's output
+    assert c(P, -1, 16, 0, P, P, None, P, *good, P, None) == SHAPE
+    assert c(*good, P, 4, 24, 0, P, P, None, P, P, None) == ALIGN          # b's cols % 16
+    assert c(PU, 4, 16, 0, P, P, None, P, *good, P, None) == ALIGN
+    assert c(*good, P, 4, 16, 0, P, P, PU, P, P, None) == ALIGN            # b's scale
+    assert c(P, 4, 16, 2, P, P, None, P, *good, P, None) == UNSUP
+    assert c(*good, P, 4, 16, 5, P, P, None, P, P, None) == UNSUP
+    assert c(P, 4, 16, 0, P, P, None, P, *good, None, None) == NULL     # workspace
     # a is checked before b
-    assert c(P, 4, 16, 2, P, P, None, P, P, 4, 24, 0, P, P, None, P, None) == UNSUP
+    assert c(P, 4, 16, 2, P, P, None, P, P, 4, 24, 0, P, P, None, P, P, None) == UNSUP
 
 
 def test_f32_input_errors(L):
     a = L.fp8_amax_f32
-    assert a(P, 4, 16, 0, None, None, None, None) == NULL
-    assert a(P, -1, 16, 0, P, None, None, None) == SHAPE
-    assert a(PU, 4, 16, 0, P, None, None, None) == ALIGN
-    assert a(P, 4, 16, 3, P, None, None, None) == UNSUP
+    assert a(P, 4, 16, 0, None, None, None, P, None) == NULL
+    assert a(P, 4, 16, 0, P, None, None, None, None) == NULL             # workspace
+    assert a(P, -1, 16, 0, P, None, None, P, None) == SHAPE
+    assert a(PU, 4, 16, 0, P, None, None, P, None) == ALIGN
+    assert a(P, 4, 16, 3, P, None, None, P, None) == UNSUP
     q = L.fp8_quantize_tensor_f32
-    assert q(P, 4, 24, 0, P, P, None, None, None) == ALIGN               # cols % 16
-    assert q(P, 8, 16, 0, P, P, P, None, None) == ALIGN                  # qT needs rows % 16
-    assert q(None, 4, 16, 0, P, P, None, None, None) == NULL
+    assert q(P, 4, 24, 0, P, P, None, None, None, None) == ALIGN         # cols % 16
+    assert q(P, 8, 16, 0, P, P, P, None, None, None) == ALIGN            # qT needs rows % 16
+    assert q(None, 4, 16, 0, P, P, None, None, None, None) == NULL
+    assert q(P, 16, 16, 0, P, P, None, P, None, None) == NULL            # amax_out, no workspace
 
 
 def test_transposed_block_and_mx_errors(L):
@@ -166,11 +185,13 @@ def test_gemm_errors(L):
     assert g(r(t), r(t), 16, 16, 16, PU, None) == ALIGN
     assert g(r(_op(0, 0, data=PU)), r(t), 16, 16, 16, P, None) == ALIGN
     ff = L.fp8_gemm_fprop_fused
-    assert ff(r(t), r(t), 16, 16, 16, P, 0, P, None, None, None) == NULL     # nothing fused
-    assert ff(r(t), r(t), 16, 16, 16, P, 0, None, P, None, None) == NULL     # y_q without scale
-    assert ff(r(t), r(t), 16, 16, 16, P, 5, P, P, None, None) == UNSUP       # y_fmt
-    assert ff(r(t), r(t), 16, 24, 16, P, 0, P, P, None, None) == ALIGN       # N % 16
-    assert ff(r(t), r(t), 16, 16, 16, None, 0, P, None, P, None) == NULL     # amax only, no y
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, P, None, None, None, None) == NULL   # nothing fused
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, None, P, None, None, None) == NULL   # y_q, no scale
+    assert ff(r(t), r(t), 16, 16, 16, P, 5, P, P, None, None, None) == UNSUP     # y_fmt
+    assert ff(r(t), r(t), 16, 24, 16, P, 0, P, P, None, None, None) == ALIGN     # N % 16
+    assert ff(r(t), r(t), 16, 16, 16, None, 0, P, None, P, P, None) == NULL      # amax only, no y
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, None, None, P, None, None) == NULL   # amax, no ws
+    assert ff(r(t), r(t), 16, 16, 16, P, 0, None, None, P, P + 32, None) == ALIGN
     wf = L.fp8_gemm_wgrad_f32
     assert wf(r(t), r(t), 16, 16, 16, P, 2, None) == UNSUP             # accumulate flag
     assert wf(r(t), r(t), 24, 16, 16, P, 0, None) == ALIGN             # M % 16

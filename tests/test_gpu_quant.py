@@ -196,10 +196,11 @@ def test_quantize_tensor_current_concurrent_streams(F, orc):
     streams = [torch.cuda.Stream() for _ in xs]
     outs = [(empty_dev(shape, torch.uint8),) + tuple(empty_dev(1, torch.float32) for _ in range(3))
             for _ in xs]
+    wss = [F.workspace() for _ in xs]            # one workspace per stream
     torch.cuda.synchronize()
     for _ in range(3):
-        for x, st, (q, am, s, si) in zip(dx, streams, outs):
-            F.fp8_quantize_tensor_current(x, E4M3, q, None, am, s, si, stream=st)
+        for x, st, (q, am, s, si), ws in zip(dx, streams, outs, wss):
+            F.fp8_quantize_tensor_current(x, E4M3, q, None, am, s, si, stream=st, workspace=ws)
     torch.cuda.synchronize()
     for x, (q, am, s, si) in zip(xs, outs):
         wa = orc.amax(x)
@@ -243,6 +244,7 @@ def test_quantize_pair_current(F, orc, sa, sb, fa, fb):
     (one with a NaN) and a single-tensor call in between, so each call starts
     from the words the previous one left."""
     outs = (_current_outputs(sa), _current_outputs(sb))
+    ws = F.workspace()
     for rep in range(3):
         xa = rand_bits(sa, 900 + 10 * rep + sa[1], 2.0, specials=True)
         xb = rand_bits(sb, 901 + 10 * rep + sb[1], 0.02, specials=True)
@@ -250,11 +252,12 @@ def test_quantize_pair_current(F, orc, sa, sb, fa, fb):
             xb.reshape(-1)[xb.size // 2] = 0x7FC0                      # NaN: amax NaN, scale 1
         da = dev_bf16(xa) if xa.size else torch.empty(sa, dtype=torch.bfloat16, device=DEV)
         db = dev_bf16(xb) if xb.size else torch.empty(sb, dtype=torch.bfloat16, device=DEV)
-        F.fp8_quantize_pair_current(da, fa, *outs[0], db, fb, *outs[1])
+        F.fp8_quantize_pair_current(da, fa, *outs[0], db, fb, *outs[1], workspace=ws)
         if rep == 1:
             one = _current_outputs((64, 64))
             x1 = rand_bits((64, 64), 77, 1.0)
-            F.fp8_quantize_tensor_current(dev_bf16(x1), E4M3, one[0], None, *one[1:])
+            F.fp8_quantize_tensor_current(dev_bf16(x1), E4M3, one[0], None, *one[1:],
+                                          workspace=ws)
         torch.cuda.synchronize()
         _check_current(orc, xa, fa, *outs[0], label=f"a rep {rep}")
         _check_current(orc, xb, fb, *outs[1], label=f"b rep {rep}")
@@ -479,11 +482,44 @@ def test_quantize_pair_current_concurrent_streams(F, orc):
     dx = [[dev_bf16(x) for x in pair] for pair in xs]
     outs = [[_current_outputs(sh) for sh in shapes] for _ in range(2)]
     streams = [torch.cuda.Stream() for _ in range(2)]
+    wss = [F.workspace() for _ in range(2)]      # one workspace per stream
     torch.cuda.synchronize()
     for _ in range(3):
-        for d, o, st in zip(dx, outs, streams):
-            F.fp8_quantize_pair_current(d[0], E4M3, *o[0], d[1], E4M3, *o[1], stream=st)
+        for d, o, st, ws in zip(dx, outs, streams, wss):
+            F.fp8_quantize_pair_current(d[0], E4M3, *o[0], d[1], E4M3, *o[1], stream=st,
+                                        workspace=ws)
     torch.cuda.synchronize()
     for i in range(2):
         for j in range(2):
             _check_current(orc, xs[i][j], E4M3, *outs[i][j], label=f"stream {i} tensor {j}")
+
+
+@pytest.mark.parametrize("calls", ["one", "pair"])
+def test_current_scaling_wait_bound_fallback(F, orc, calls):
+    """The one-launch current scaling with its grid-wide wait bounded to one
+    poll (fp8_workspace_init's wait_polls = 1): nearly every workgroup gives
+    up waiting and takes the fallback, reducing the whole input itself.  The
+    results are still the oracle's, bit for bit, over three calls in a row on
+    one workspace (the counters the fallback leaves are consistent), and a
+    workspace with the default bound then gives the same bytes."""
+    shapes = ((4096, 4096), (11008, 4096))
+    xs = [rand_bits(sh, 950 + j, 2.0 if j == 0 else 0.02) for j, sh in enumerate(shapes)]
+    dx = [dev_bf16(x) for x in xs]
+    ws1 = F.workspace(wait_polls=1)
+    for rep in range(3):
+        outs = [_current_outputs(sh) for sh in shapes]
+        if calls == "pair":
+            F.fp8_quantize_pair_current(dx[0], E4M3, *outs[0], dx[1], E4M3, *outs[1],
+                                        workspace=ws1)
+        else:
+            for d, o in zip(dx, outs):
+                F.fp8_quantize_tensor_current(d, E4M3, o[0], None, *o[1:], workspace=ws1)
+        torch.cuda.synchronize()
+        for j in range(2):
+            _check_current(orc, xs[j], E4M3, *outs[j], label=f"{calls} rep {rep} tensor {j}")
+    ref = [_current_outputs(sh) for sh in shapes]
+    F.fp8_quantize_pair_current(dx[0], E4M3, *ref[0], dx[1], E4M3, *ref[1],
+                                workspace=F.workspace())
+    torch.cuda.synchronize()
+    for j in range(2):
+        assert np.array_equal(bytes8(ref[j][0]), bytes8(outs[j][0]))
