@@ -38,36 +38,8 @@ namespace w8 {
 
 constexpr int BM = 256, BN = 256, NT = 512, NW = 8;
 constexpr int WM = 64, WN = 128;           // wave sub-tile
-constexpr int NF = WM / 16, NJ = WN / 16;  // fragments per wave: 4 (M) x 8 (N)
 
-// Per-row scale words of one operand for four steps: wave `part` (0..3)
-// moves rows 64*part .. 64*part + 63 of the tile, 16 bytes per row (the words
-// of steps 4c .. 4c+3), landing at LDS words 4*row .. 4*row + 3.
-//   block: the FP32 scales of the row's 128-K blocks (rows grouped by BR:
-//          BR = 1 one scale per row, BR = 128 one per 128 rows);
-//   MX:    the dwords holding the row's four E8M0 bytes of each step.
-// One 16-byte load per row and four steps rather than a 4-byte load per step
-// cuts the scale requests, which touch one cache line per row, by four.
-// Rows past the matrix edge, and words past the scale array, read past the
-// descriptor range and get 0; words past the row's last step are not used.
-struct ScaleRows {
-  v4i rsrc;
-  int voff;
-  uint32_t records;
-  __device__ __forceinline__ void init(const void* scales, int64_t row0, int64_t rows_left,
-                                       int br, int64_t words_per_row, int part) {
-    const int64_t first = row0 / br;
-    const int64_t rows = rows_left < 256 ? rows_left : 256;
-    const int64_t groups = (rows + br - 1) / br;
-    records = (uint32_t)(groups * words_per_row * 4);
-    rsrc = make_rsrc(static_cast<const uint8_t*>(scales) + first * words_per_row * 4, records);
-    const int r = part * 64 + (int)(threadIdx.x & 63);
-    voff = r < rows ? (int)((r / br) * words_per_row * 4) : -1;
-  }
-  __device__ __forceinline__ void load(uint32_t lds, int chunk) const {
-    dma16(rsrc, lds, voff >= 0 ? voff + chunk * 16 : (int)records);
-  }
-};
+constexpr int NF = WM / 16, NJ = WN / 16;  // fragments per wave: 4 (M) x 8 (N)
 
 // Blockwise promotion of fragment column j: acc[f][j] += s(f, r) * P[f], the
 // 128-K partial products of this step times their FP32 scale product.
@@ -95,7 +67,13 @@ __device__ __forceinline__ void promote(v4f (&acc)[NF][NJ], const v4f (&P)[NF],
   }
 }
 
-template <int MODE, int FA, int FB, int BRA, int BRB>
+// SPREAD: the next step's tile loads are issued over the first SPREAD
+// fragment columns of a step (1: all at its start).  Spreading keeps the
+// texture-address FIFO from filling (both waves of a SIMD would stall on it
+// at once) but gives the last loads less time before the step's barrier:
+// +5-8 % on the LLaMA2-7B up-projection (K = 4096), -3 to -5 % where the
+// long-K operand panels come from the infinity cache or HBM (K >= 5120).
+template <int MODE, int FA, int FB, int BRA, int BRB, int SPREAD = 1>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm8(Args p) {
   constexpr bool SCALED = MODE != kTensor;
@@ -104,6 +82,8 @@ void k_gemm8(Args p) {
   // per chunk of four steps: row r's words at 4r .. 4r+3; rows 0..255 = A,
   // 256..511 = B
   __shared__ __attribute__((aligned(16))) uint32_t lS[SCALED ? 2 : 1][SCALED ? 2048 : 4];
+  // where the scale DMA of a step that starts no chunk lands (zeros)
+  __shared__ __attribute__((aligned(16))) uint32_t lS_idle[SCALED && SPREAD > 1 ? 256 : 4];
   int tm, tn;
   if (!tile_coords(p, tm, tn)) return;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -139,6 +119,29 @@ void k_gemm8(Args p) {
       if ((kt & 3) == 0)
         ls.load(lds_addr(&lS[(kt >> 2) & 1][((w & 3) * 64 + (w >> 2) * 256) * 4]), kt >> 2);
   };
+  // Part `part` of SPREAD of the loads of step kt into `stage`, A and B loads
+  // alternating, without branches: live = false (no next step) or a step
+  // that starts no scale chunk reads out of range, fetching nothing
+  // (zeros land in the unused stage, or in lS_idle).
+  constexpr int NLD = 2 * TileLoader<BM, NW>::L;
+  auto issue_part = [&](int stage, int kt, int part, bool live) {
+#pragma unroll
+    for (int i = part * NLD / SPREAD; i < (part + 1) * NLD / SPREAD; ++i) {
+      if (i & 1)
+        lb.load_one(lB[stage], (int64_t)kt * BK, i >> 1, live);
+      else
+        la.load_one(lA[stage], (int64_t)kt * BK, i >> 1, live);
+    }
+    if constexpr (SCALED) {
+      if (part == 0) {
+        const bool chunk = live && (kt & 3) == 0;
+        const uint32_t to = lds_addr(&lS[(kt >> 2) & 1][((w & 3) * 64 + (w >> 2) * 256) * 4]);
+        const uint32_t idle = lds_addr(&lS_idle[0]);
+        const uint32_t m = 0u - (uint32_t)chunk;
+        ls.load((to & m) | (idle & ~m), kt >> 2, chunk);
+      }
+    }
+  };
 
   if (nk > 0) issue(0, 0);
   wait_vm<0>();
@@ -172,12 +175,16 @@ void k_gemm8(Args p) {
       for (int f = 0; f < NF; ++f) ea[f] = S[((wm * WM + f * 16 + lr) * 4 + sw) * 4 + g];
       eb[0] = S[((256 + wn * WN + lr) * 4 + sw) * 4 + g];
     }
-    if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
+    if constexpr (SPREAD == 1) {
+      if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     v4f P[2][NF];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      if constexpr (SPREAD > 1)
+        if (j < SPREAD) issue_part(cur ^ 1, kt + 1, j, kt + 1 < nk);
       if (j + 1 < NJ) bf[(j + 1) & 1] = load_frag(Bs, wn * WN + (j + 1) * 16);
       if constexpr (MODE == kMX) {
         // the next column's B scale byte, one column ahead like its fragment
@@ -265,7 +272,7 @@ void k_gemm8(Args p) {
   tile_amax<NT>(p, tm, tn, mx, red);
 }
 
-template <int MODE, int FA, int FB, int BRA, int BRB>
+template <int MODE, int FA, int FB, int BRA, int BRB, int SPREAD = 1>
 hipError_t run(const GemmProblem& q, hipStream_t s) {
   Args a;
   a.A = q.A; a.B = q.B; a.sa = q.sa; a.sb = q.sb; a.C = q.C; a.out = q.out;
@@ -273,17 +280,17 @@ hipError_t run(const GemmProblem& q, hipStream_t s) {
   a.M = q.M; a.N = q.N; a.K = q.K;
   a.tiles_m = (int)((q.M + BM - 1) / BM);
   a.tiles_n = (int)((q.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm8<MODE, FA, FB, BRA, BRB>), dim3(grid_for_tiles(a.tiles_m * a.tiles_n)),
+  hipLaunchKernelGGL((k_gemm8<MODE, FA, FB, BRA, BRB, SPREAD>), dim3(grid_for_tiles(a.tiles_m * a.tiles_n)),
                      dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int MODE, int BRA, int BRB>
+template <int MODE, int BRA, int BRB, int SPREAD = 1>
 hipError_t run_fmt(const GemmProblem& q, hipStream_t s) {
-  if (q.fa == kE4M3 && q.fb == kE4M3) return run<MODE, kE4M3, kE4M3, BRA, BRB>(q, s);
-  if (q.fa == kE5M2 && q.fb == kE4M3) return run<MODE, kE5M2, kE4M3, BRA, BRB>(q, s);
-  if (q.fa == kE4M3 && q.fb == kE5M2) return run<MODE, kE4M3, kE5M2, BRA, BRB>(q, s);
-  return run<MODE, kE5M2, kE5M2, BRA, BRB>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE4M3) return run<MODE, kE4M3, kE4M3, BRA, BRB, SPREAD>(q, s);
+  if (q.fa == kE5M2 && q.fb == kE4M3) return run<MODE, kE5M2, kE4M3, BRA, BRB, SPREAD>(q, s);
+  if (q.fa == kE4M3 && q.fb == kE5M2) return run<MODE, kE4M3, kE5M2, BRA, BRB, SPREAD>(q, s);
+  return run<MODE, kE5M2, kE5M2, BRA, BRB, SPREAD>(q, s);
 }
 
 }  // namespace w8
@@ -301,7 +308,7 @@ hipError_t launch_gemm(const GemmProblem& q0, hipStream_t s) {
   q.part = q.amax ? q.ws : nullptr;   // per-tile maxima in the caller's workspace
   hipError_t err;
   if (q.mode == kTensor)
-    err = w8::run_fmt<kTensor, 1, 1>(q, s);
+    err = q.K <= 4096 ? w8::run_fmt<kTensor, 1, 1, 4>(q, s) : w8::run_fmt<kTensor, 1, 1>(q, s);
   else if (q.mode == kMX)
     err = q.K % 128 != 0 ? launch_gemm_mx_k32(q, s) : w8::run_fmt<kMX, 1, 1>(q, s);
   else if (q.bra == 1 && q.brb == 128)

@@ -143,14 +143,50 @@ struct TileLoader {
     }
   }
 
-  __device__ __forceinline__ void load(const uint8_t* tile, int64_t k0) const {
-    const bool kin = k0 + kchunk * 16 < K;
-    const uint32_t base = lds_addr(tile) + (uint32_t)(w * L * 1024);
+  // live = false: every lane reads past the range, so the hardware fetches
+  // nothing and zero-fills the tile (a load that need not happen, issued
+  // without a branch around it).
+  __device__ __forceinline__ void load(const uint8_t* tile, int64_t k0, bool live = true) const {
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int off = kin ? voff[i] + (int)k0 : (int)records;
-      dma16(rsrc, base + i * 1024, off);
-    }
+    for (int i = 0; i < L; ++i) load_one(tile, k0, i, live);
+  }
+  // The i-th of this wave's L loads of the tile (so that a step's loads can
+  // be spread over its MFMAs).
+  __device__ __forceinline__ void load_one(const uint8_t* tile, int64_t k0, int i,
+                                           bool live = true) const {
+    const bool kin = live && k0 + kchunk * 16 < K;
+    const uint32_t base = lds_addr(tile) + (uint32_t)(w * L * 1024);
+    dma16(rsrc, base + i * 1024, kin ? voff[i] + (int)k0 : (int)records);
+  }
+};
+
+// Per-row scale words of one operand for four steps: wave `part` (0..3)
+// moves rows 64*part .. 64*part + 63 of the tile, 16 bytes per row (the words
+// of steps 4c .. 4c+3), landing at LDS words 4*row .. 4*row + 3.
+//   block: the FP32 scales of the row's 128-K blocks (rows grouped by BR:
+//          BR = 1 one scale per row, BR = 128 one per 128 rows);
+//   MX:    the dwords holding the row's four E8M0 bytes of each step.
+// One 16-byte load per row and four steps rather than a 4-byte load per step
+// cuts the scale requests, which touch one cache line per row, by four.
+// Rows past the matrix edge, and words past the scale array, read past the
+// descriptor range and get 0; words past the row's last step are not used.
+struct ScaleRows {
+  v4i rsrc;
+  int voff;
+  uint32_t records;
+  __device__ __forceinline__ void init(const void* scales, int64_t row0, int64_t rows_left,
+                                       int br, int64_t words_per_row, int part) {
+    const int64_t first = row0 / br;
+    const int64_t rows = rows_left < 256 ? rows_left : 256;
+    const int64_t groups = (rows + br - 1) / br;
+    records = (uint32_t)(groups * words_per_row * 4);
+    rsrc = make_rsrc(static_cast<const uint8_t*>(scales) + first * words_per_row * 4, records);
+    const int r = part * 64 + (int)(threadIdx.x & 63);
+    voff = r < rows ? (int)((r / br) * words_per_row * 4) : -1;
+  }
+  // live = false: nothing is fetched and zeros land at `lds`
+  __device__ __forceinline__ void load(uint32_t lds, int chunk, bool live = true) const {
+    dma16(rsrc, lds, live && voff >= 0 ? voff + chunk * 16 : (int)records);
   }
 };
 
