@@ -191,7 +191,8 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
       !aligned(workspace, 256))
     return FP8_ERR_ALIGN;
   return hip(fp8sg::launch_quantize_current(x_bf16, rows, cols, fmt, q, qT, amax, scale,
-                                            scale_inv, wsp(workspace), st(stream), 0));
+                                            scale_inv, fp8sg::current_ws(wsp(workspace)),
+                                            st(stream), 0));
 }
 
 static fp8_status_t current_ok(const void* x, int64_t rows, int64_t cols, int32_t fmt,

@@ -26,6 +26,23 @@ constexpr int kConfigWords = 32;
 constexpr int kGridWordsAt = kWorkspaceWords;
 constexpr int kConfigAt = kWorkspaceWords + kGridMaxWords;
 constexpr int kWorkspaceTotalWords = kConfigAt + kConfigWords;
+// Partial maxima of one quantise launch (its largest grid), and the words of
+// one grid-wide maximum (a counter and a maximum line per group of 32
+// workgroups, a flag line per group, the top counter and maximum line).
+constexpr int kMaxPartials = 2048;
+constexpr int kGridSetWords = (2 * (kMaxPartials / 32) + 1) * 32;
+// Where one current-scaling call reduces: kMaxPartials partial maxima, one
+// set of grid-wide maximum words (zero before first use, left zero), and
+// the config word (the wait bound, 0 = default).
+struct CurrentWs {
+  uint32_t* part;
+  uint32_t* grid;
+  const uint32_t* cfg;
+};
+inline CurrentWs current_ws(uint32_t* ws) {
+  return CurrentWs{ws, ws + kGridWordsAt, ws + kConfigAt};
+}
+
 // Clear a workspace for first use and set its wait bound (a fill kernel).
 hipError_t launch_workspace_init(uint32_t* ws, uint32_t wait_polls, hipStream_t s);
 // amax[0] = the largest of part[0 .. n-1], as an FP32 value.
@@ -42,7 +59,7 @@ hipError_t launch_quantize_tensor(const void* x, int64_t rows, int64_t cols, int
 // a grid the device holds at once, else two.
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
-                                   float* scale_inv, uint32_t* ws, hipStream_t s, int in);
+                                   float* scale_inv, const CurrentWs& ws, hipStream_t s, int in);
 // One BF16 tensor under current scaling, without a transposed copy.
 struct CurrentTensor {
   const void* x;

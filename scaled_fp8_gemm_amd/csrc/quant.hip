@@ -24,8 +24,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Workgroups of a partial-producing launch (the partial buffer's length).
-constexpr int kMaxPartials = 2048;
 
 // Streaming kernels walk the tensor in contiguous chunks of 16 KB per
 // workgroup (kChunkLoads 16-byte loads per thread in flight), chunk c going to
@@ -262,8 +260,9 @@ constexpr int kLine = 32;                             // words per 128-byte line
 constexpr int kGroup = 32;                            // workgroups per group
 constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
 constexpr uint32_t kNoMax = 0xFFFFFFFFu;              // above any magnitude: the wait ran out
-// words of one grid-wide maximum; the paired launch uses two such sets
-constexpr int kGridSetWords = (2 * kMaxGroups + 1) * kLine;
+// words of one grid-wide maximum (kGridSetWords); the paired launch uses two
+// such sets
+static_assert(kGridSetWords == (2 * kMaxGroups + 1) * kLine, "grid-wide maximum words");
 static_assert(2 * kGridSetWords <= kGridMaxWords, "grid-wide maximum words");
 __device__ __forceinline__ uint32_t* gm_cnt(uint32_t* w, int g) { return w + g * kLine; }
 __device__ __forceinline__ uint32_t* gm_max(uint32_t* w, int g) { return w + g * kLine + 1; }
@@ -1230,7 +1229,7 @@ static int coop_capacity() {
 // far more than the pass it saves; the grid maximum's bounded wait covers
 // the rare grid that is not all resident.)
 template <int FMT, int U>
-static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_t* ws,
+static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, const CurrentWs& ws,
                                 float* amax, float* scale, float* scale_inv, hipStream_t s,
                                 bool* done) {
   const int64_t g = (nvec + (int64_t)U * kThreads - 1) / ((int64_t)U * kThreads);
@@ -1239,7 +1238,7 @@ static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_
   const uint4* xv = static_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(q);
   hipLaunchKernelGGL((k_amax_cast<FMT, U>), dim3((unsigned)g), dim3(kThreads), 0, s, xv, nvec,
-                     qv, ws + kGridWordsAt, ws + kConfigAt, amax, scale, scale_inv);
+                     qv, ws.grid, ws.cfg, amax, scale, scale_inv);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) *done = true;
   return err;
@@ -1247,10 +1246,10 @@ static hipError_t try_amax_cast(const void* x, int64_t nvec, uint8_t* q, uint32_
 
 hipError_t launch_quantize_current(const void* x, int64_t rows, int64_t cols, int fmt,
                                    uint8_t* q, uint8_t* qT, float* amax, float* scale,
-                                   float* scale_inv, uint32_t* ws, hipStream_t s, int in) {
+                                   float* scale_inv, const CurrentWs& ws, hipStream_t s, int in) {
   const int64_t n = rows * cols;
-  if (n == 0) return launch_amax(x, 0, fmt, amax, scale, scale_inv, ws, s, in);
-  uint32_t* part = ws;
+  if (n == 0) return launch_amax(x, 0, fmt, amax, scale, scale_inv, ws.part, s, in);
+  uint32_t* part = ws.part;
   hipError_t err = hipSuccess;
   // One launch when the tensor fits the registers of a co-resident grid:
   // BF16, whole 16-byte vectors, no transposed copy.
@@ -1353,10 +1352,10 @@ hipError_t launch_quantize_pair_current(const CurrentTensor& ta, const CurrentTe
   }
   // an empty tensor, or a pair the device cannot hold at once: one call each
   hipError_t err = launch_quantize_current(ta.x, ta.rows, ta.cols, ta.fmt, ta.q, nullptr, ta.amax,
-                                           ta.scale, ta.scale_inv, ws, s, kInBF16);
+                                           ta.scale, ta.scale_inv, current_ws(ws), s, kInBF16);
   if (err != hipSuccess) return err;
   return launch_quantize_current(tb.x, tb.rows, tb.cols, tb.fmt, tb.q, nullptr, tb.amax, tb.scale,
-                                 tb.scale_inv, ws, s, kInBF16);
+                                 tb.scale_inv, current_ws(ws), s, kInBF16);
 }
 
 hipError_t launch_amax_finalize(const uint32_t* part, int n, float* amax, hipStream_t s) {
