@@ -168,6 +168,28 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
                                          float* scale, float* scale_inv, void* workspace,
                                          void* stream);
 
+/* fp8_quantize_tensor_current for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same results, but no workspace argument.  The
+ * call reduces through a static scratch array of the library, 24832 bytes
+ * per GPU (2048 partial maxima, 65 lines of grid-wide maximum words, one
+ * settings line), held from the first call on a GPU until the process ends;
+ * that first call takes the array's device address and clears it with a
+ * kernel on `stream`.  The scratch suffices for every tensor the regular
+ * call accepts (a quantise launch writes at most 2048 partial maxima
+ * whatever the tensor's size), so no size is rejected for it; the wait
+ * bound is the default one.  All calls on one GPU share the array and each
+ * leaves it ready for the next: calls ordered on one stream are safe, calls
+ * that may overlap on one GPU (other streams, concurrent graph replays)
+ * race and must not be made.  Nothing is allocated: no hipMalloc, hipFree
+ * or allocating library routine.
+ * Arguments and errors as fp8_quantize_tensor_current (without workspace);
+ * FP8_ERR_HIP also reports a failure to find or clear the scratch. */
+fp8_status_t fp8_quantize_tensor_current_noalloc(const void* x_bf16, int64_t rows, int64_t cols,
+                                                 int32_t fmt, uint8_t* q, uint8_t* qT,
+                                                 float* amax, float* scale, float* scale_inv,
+                                                 void* stream);
+
 /* Per-tensor current scaling of a GEMM's two operands (for instance X and W
  * of fprop) in one call: the results are exactly those of
  * fp8_quantize_tensor_current on each tensor without a transposed copy

@@ -195,6 +195,28 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
                                             st(stream), 0));
 }
 
+fp8_status_t fp8_quantize_tensor_current_noalloc(const void* x_bf16, int64_t rows, int64_t cols,
+                                                 int32_t fmt, uint8_t* q, uint8_t* qT,
+                                                 float* amax, float* scale, float* scale_inv,
+                                                 void* stream) {
+  if (!amax || !scale_inv) return FP8_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8_ERR_UNSUPPORTED;
+  if (!dims_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (!have(x_bf16, rows * cols) || !have(q, rows * cols)) return FP8_ERR_NULL;
+  if (cols % 16) return FP8_ERR_ALIGN;
+  if (qT && rows % 16) return FP8_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || (qT && !aligned(qT, 16)) ||
+      !aligned(amax, 4) || !aligned(scale_inv, 4) || (scale && !aligned(scale, 4)))
+    return FP8_ERR_ALIGN;
+  // the static scratch holds what any tensor needs: a quantise launch writes
+  // at most kMaxPartials partial maxima, whatever its size
+  fp8sg::CurrentWs ws;
+  const hipError_t err = fp8sg::noalloc_scratch(st(stream), &ws);
+  if (err != hipSuccess) return FP8_ERR_HIP;
+  return hip(fp8sg::launch_quantize_current(x_bf16, rows, cols, fmt, q, qT, amax, scale,
+                                            scale_inv, ws, st(stream), 0));
+}
+
 static fp8_status_t current_ok(const void* x, int64_t rows, int64_t cols, int32_t fmt,
                                const uint8_t* q, const float* amax, const float* scale,
                                const float* scale_inv) {

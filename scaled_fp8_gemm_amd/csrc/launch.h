@@ -42,6 +42,12 @@ struct CurrentWs {
 inline CurrentWs current_ws(uint32_t* ws) {
   return CurrentWs{ws, ws + kGridWordsAt, ws + kConfigAt};
 }
+// The library's static scratch on the current device (for
+// fp8_quantize_tensor_current_noalloc): kScratchWords words laid out as a
+// CurrentWs.  The first call on a device takes its address and clears it
+// with a kernel on `s`; nothing is allocated.
+constexpr int kScratchWords = kMaxPartials + kGridSetWords + kConfigWords;
+hipError_t noalloc_scratch(hipStream_t s, CurrentWs* out);
 
 // Clear a workspace for first use and set its wait bound (a fill kernel).
 hipError_t launch_workspace_init(uint32_t* ws, uint32_t wait_polls, hipStream_t s);

@@ -14,6 +14,7 @@
 // workgroups serialise (about 10 ns each on MI355X) and would cost more than
 // the pass itself.
 #include <atomic>
+#include <mutex>
 
 #include "fp8_device.h"
 #include "launch.h"
@@ -1082,6 +1083,46 @@ __global__ __launch_bounds__(kThreads) void k_workspace_init(uint32_t* __restric
 hipError_t launch_workspace_init(uint32_t* ws, uint32_t wait_polls, hipStream_t s) {
   hipLaunchKernelGGL(k_workspace_init, dim3(64), dim3(kThreads), 0, s, ws, wait_polls);
   return hipGetLastError();
+}
+
+// Static scratch of fp8_quantize_tensor_current_noalloc, for callers that
+// cannot allocate: partial maxima, one set of grid-wide maximum words, the
+// config word (kScratchWords words, 24.8 KB per device, held until the
+// process ends).  Every GPU has its own copy at its own address; host code
+// uses only the address hipGetSymbolAddress returns for the current device
+// (the symbol's name is a host-side stand-in, not a device address).
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+static_assert(kMaxPartials % 32 == 0, "grid words start on a 128-byte line");
+
+__global__ __launch_bounds__(kThreads) void k_zero_words(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0u;
+}
+
+hipError_t noalloc_scratch(hipStream_t s, CurrentWs* out) {
+  static std::mutex mu;
+  static uint32_t* ptr[64];   // per device, set once
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    // the grid-wide maximum's counters, maxima and flags start at zero, and
+    // a zero config word selects the default wait bound (static storage
+    // starts zeroed; this clears it again on the caller's stream, with a
+    // kernel rather than a memset so that a first call may be captured)
+    hipLaunchKernelGGL(k_zero_words, dim3(8), dim3(kThreads), 0, s, static_cast<uint32_t*>(p),
+                       kScratchWords);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  uint32_t* w = ptr[dev];
+  *out = CurrentWs{w, w + kMaxPartials, w + kMaxPartials + kGridSetWords};
+  return hipSuccess;
 }
 
 int device_cu_count() {

@@ -66,6 +66,7 @@ def lib():
             "fp8_quantize_tensor": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
             "fp8_amax_f32": [vp, i64, i64, i32, vp, vp, vp, vp, vp],
             "fp8_quantize_tensor_current": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp],
+            "fp8_quantize_tensor_current_noalloc": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
             "fp8_quantize_pair_current": [vp, i64, i64, i32, vp, vp, vp, vp,
                                           vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
             "fp8_quantize_tensor_f32": [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp],
@@ -200,6 +201,19 @@ def fp8_quantize_tensor_current(x, fmt, q, qT, amax, scale, scale_inv, stream=No
                                              _t(scale, "scale", _F32, 1, True),
                                              _t(scale_inv, "scale_inv", _F32, 1), ws.ptr,
                                              _stream(stream)))
+
+
+def fp8_quantize_tensor_current_noalloc(x, fmt, q, qT, amax, scale, scale_inv, stream=None):
+    """fp8_quantize_tensor_current through the library's static scratch: no
+    workspace, nothing allocated (calls that overlap on one GPU race)."""
+    rows, cols = _rc(x)
+    n = rows * cols
+    _check("fp8_quantize_tensor_current_noalloc",
+           lib().fp8_quantize_tensor_current_noalloc(
+               _t(x, "x", _BF16, n), rows, cols, fmt, _t(q, "q", _U8, n),
+               _t(qT, "qT", _U8, n, True), _t(amax, "amax", _F32, 1),
+               _t(scale, "scale", _F32, 1, True), _t(scale_inv, "scale_inv", _F32, 1),
+               _stream(stream)))
 
 
 def fp8_quantize_pair_current(a, fmt_a, qa, amax_a, scale_a, scale_inv_a,
