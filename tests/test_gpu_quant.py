@@ -474,8 +474,9 @@ def test_quantize_pair_current_concurrent_streams(F, orc):
     """Two paired one-launch calls running at once on different streams, each
     grid as large as the device holds (the LLaMA2-7B up-projection's X and W):
     however the grids interleave, every tensor's amax, scale pair and bytes
-    are the oracle's (a workgroup whose grid-wide wait runs out reduces its
-    tensor itself)."""
+    are the oracle's (when a grid-wide wait runs out, one workgroup completes
+    the amax from the maxima already in and the inputs of the workgroups that
+    have not arrived, and publishes it)."""
     shapes = ((4096, 4096), (11008, 4096))
     xs = [[rand_bits(sh, 800 + 10 * i + j, 2.0 if j == 0 else 0.02) for j, sh in enumerate(shapes)]
           for i in range(2)]
@@ -494,16 +495,27 @@ def test_quantize_pair_current_concurrent_streams(F, orc):
             _check_current(orc, xs[i][j], E4M3, *outs[i][j], label=f"stream {i} tensor {j}")
 
 
+@pytest.mark.parametrize("spike", [None, "first", "middle", "last"])
 @pytest.mark.parametrize("calls", ["one", "pair"])
-def test_current_scaling_wait_bound_fallback(F, orc, calls):
+def test_current_scaling_wait_bound_fallback(F, orc, calls, spike):
     """The one-launch current scaling with its grid-wide wait bounded to one
-    poll (fp8_workspace_init's wait_polls = 1): nearly every workgroup gives
-    up waiting and takes the fallback, reducing the whole input itself.  The
-    results are still the oracle's, bit for bit, over three calls in a row on
-    one workspace (the counters the fallback leaves are consistent), and a
-    workspace with the default bound then gives the same bytes."""
+    poll (fp8_workspace_init's wait_polls = 1): workgroups give up waiting
+    almost at once, and the first of them completes the amax itself from the
+    maxima already in and the inputs of the workgroups that have not arrived
+    (or takes the published amax if all arrive meanwhile).  The results are
+    still the oracle's, bit for bit, over three calls in a row on one
+    workspace (the words each call leaves are consistent), also when one
+    element far above the rest sits in the first, a middle or the last
+    workgroup's share; a workspace with the default bound then gives the same
+    bytes."""
     shapes = ((4096, 4096), (11008, 4096))
     xs = [rand_bits(sh, 950 + j, 2.0 if j == 0 else 0.02) for j, sh in enumerate(shapes)]
+    if spike is not None:
+        for j, x in enumerate(xs):
+            flat = x.reshape(-1)
+            at = {"first": 5, "middle": flat.size // 2 + 77, "last": flat.size - 3}[spike]
+            # -300 and 3 are exact in BF16: the upper half of their FP32 bits
+            flat[at] = np.array([-300.0 if j == 0 else 3.0], np.float32).view(np.uint32)[0] >> 16
     dx = [dev_bf16(x) for x in xs]
     ws1 = F.workspace(wait_polls=1)
     for rep in range(3):
@@ -517,6 +529,8 @@ def test_current_scaling_wait_bound_fallback(F, orc, calls):
         torch.cuda.synchronize()
         for j in range(2):
             _check_current(orc, xs[j], E4M3, *outs[j], label=f"{calls} rep {rep} tensor {j}")
+            if spike is not None:
+                assert f32(outs[j][1])[0] == (300.0 if j == 0 else 3.0), (spike, j)
     ref = [_current_outputs(sh) for sh in shapes]
     F.fp8_quantize_pair_current(dx[0], E4M3, *ref[0], dx[1], E4M3, *ref[1],
                                 workspace=F.workspace())
