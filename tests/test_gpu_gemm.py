@@ -82,7 +82,10 @@ def test_block_scaled(F, orc, sca, scb, M, N, K):
     check_gemm(orc, g, A, B, E4M3, E4M3, 1, sa, sb, bra, brb, label=f"block {sca}{scb} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(600, 520, 352), (256, 256, 256), (40, 1000, 4096)])
+# (300, 700, 1664): 13 steps, so the last chunk of four steps' scales is
+# partial, with ragged row and column tiles on both operands
+@pytest.mark.parametrize("M,N,K", [(600, 520, 352), (256, 256, 256), (40, 1000, 4096),
+                                   (300, 700, 1664)])
 @pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)])
 def test_mx_scaled(F, orc, M, N, K, fa, fb):
     A = rand_codes((M, K), fa, 7 + K)
@@ -94,9 +97,12 @@ def test_mx_scaled(F, orc, M, N, K, fa, fb):
     check_gemm(orc, g, A, B, fa, fb, 2, ea, eb, label=f"mx {M}x{N}x{K} fmt {fa}{fb}")
 
 
-def test_mx_nan_scale_and_distinct_block_scales(F, orc):
-    """Every 32-block has its own scale; a NaN scale (0xFF) poisons its row."""
-    M, N, K = 64, 48, 256
+@pytest.mark.parametrize("K", [128, 256, 1024, 1536])
+def test_mx_nan_scale_and_distinct_block_scales(F, orc, K):
+    """Every 32-block has its own scale; a NaN scale (0xFF) poisons its row,
+    over one, two, eight and twelve 128-K steps (the E8M0 bytes move through
+    LDS in chunks of four steps)."""
+    M, N = 64, 48
     A = rand_codes((M, K), E4M3, 1)
     B = rand_codes((N, K), E4M3, 2)
     ea = (117 + (np.arange(M * (K // 32)) % 20)).astype(np.uint8).reshape(M, K // 32)
