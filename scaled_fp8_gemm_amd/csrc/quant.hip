@@ -236,60 +236,62 @@ __global__ __launch_bounds__(kThreads) void k_cast(const uint8_t* __restrict__ x
 // The grid-wide maximum uses device-coherent atomics only (agent-scope
 // fences would write back and invalidate whole L2s, which costs more than
 // the pass it saves).  Its words live in the caller's workspace after the
-// partials, each in a cache line of its own (kLine words), and are zero
-// between calls.  Workgroups form groups of kGroup; group g has a line with
-// its arrival mask (bit i: workgroup kGroup*g + i has arrived), its maximum
-// and its departure count, and a flag line; a top line holds the count of
-// complete groups, the grand maximum, the publish and rescue claims and the
-// count of departed groups.
-//   * arrival: a workgroup atomically maxes its maximum into its group's
-//     word and, once that has returned, sets its bit in the group's mask;
-//     the group's last arrival moves the group maximum into the top word
-//     and counts the group in; the last group's last arrival reads the top
-//     word (the amax) and publishes it;
-//   * publishing: whoever first claims the publish word (a compare-and-swap)
-//     swaps kPublished | amax into every group's flag;
-//   * waiting: the others poll their group's flag with relaxed loads (at
-//     most kGroup pollers per line, so no memory channel is flooded);
-//   * departure: after its cast a workgroup counts itself out (group, then
-//     top count), and the last one out clears every word for the next call;
-//     nothing reads them after that.
-// Every update but that clearing is a returning atomic, and each is
-// performed when it returns; a workgroup waits for all of its updates before
-// it counts itself out, so none can land after the clearing.  Same-address
-// atomics serialize, so a flat counter would cost every arrival in turn;
-// here a chain is at most kGroup + kMaxGroups long.
+// partials, each in a cache line of its own (kLine words), all zero before
+// first use.  Workgroups form groups of kGroup; group g has a line with its
+// arrival mask (bit i: workgroup kGroup*g + i has arrived) and its maximum,
+// and a flag line holding (generation, amax) as one 64-bit word; a top line
+// holds the count of complete groups, the grand maximum, the publish and
+// rescue claims and the generation of the call.
+//   * arrival: a workgroup reads the generation G, atomically maxes its
+//     maximum into its group's word and, once that has returned, sets its
+//     bit in the group's mask; the group's last arrival moves the group
+//     maximum into the top word and counts the group in; the last group's
+//     last arrival reads the top word (the amax) and publishes it;
+//   * publishing: whoever moves the publish claim from G to G + 1 (a
+//     compare-and-swap) writes (G + 1, amax) to every group's flag;
+//   * waiting: the others poll their group's flag with relaxed loads until
+//     it shows G + 1 (at most kGroup pollers per line, so no memory channel
+//     is flooded);
+//   * the last arrival then sets the rescue claim to G + 1, clears the
+//     masks, maxima and top count, and advances the generation to G + 1.
+// No word needs clearing between calls: flags and claims are tagged by the
+// generation, and every workgroup reads G before its arrival, hence before
+// the last arrival advances it.  A returning atomic has been performed when
+// it returns, and each feeds the next through a register dependency, so a
+// maximum is in place before its mask bit.  Same-address atomics serialize,
+// so a flat counter would cost every arrival in turn; here a chain is at
+// most kGroup + kMaxGroups long.
 // Rescue.  The wait is bounded: a grid that is not all resident (other work
 // holding CUs, such as a second such launch on another stream) would
-// otherwise wait for ever.  The first workgroup whose wait runs out claims
-// the rescue word and computes the amax without the missing workgroups: the
-// group maxima hold every arrived workgroup's maximum, and it reads the
-// inputs of the others itself; then it publishes.  Its waiting peers
-// proceed, finish and leave, which lets the missing workgroups run; these
-// find the flag published at once.  Other workgroups whose wait ran out
-// wait again, for the rescuer.  The first wait's bound is the workspace's
-// config word, or kSpinLimit polls (about a millisecond) when that is 0.
+// otherwise wait for ever.  The first workgroup whose wait runs out moves
+// the rescue claim from G to G + 1 and computes the amax without the
+// missing workgroups: the group maxima hold every arrived workgroup's
+// maximum, and it reads the inputs of the others itself; then it tries the
+// publish claim.  If it wins, its reads came before the last arrival's
+// claim, hence before the clearing, and its amax is complete; if it loses,
+// it takes the last arrival's.  Its waiting peers proceed, finish and
+// leave, which lets the missing workgroups run; these find the flag
+// published at once.  Other workgroups whose wait ran out wait again, for
+// the rescuer.  The first wait's bound is the workspace's config word, or
+// kSpinLimit polls (about a millisecond) when that is 0.
 constexpr uint32_t kSpinLimit = 1u << 12;
 constexpr uint32_t kRescueSpinLimit = 1u << 20;       // the rescuer is running
 constexpr int kLine = 32;                             // words per 128-byte line
 constexpr int kGroup = 32;                            // workgroups per group (mask bits)
 constexpr int kMaxGroups = kMaxPartials / kGroup;     // 64
 constexpr uint32_t kNoMax = 0xFFFFFFFFu;              // above any magnitude: the wait ran out
-constexpr uint32_t kPublished = 0x80000000u;          // above any magnitude's bits
 // words of one grid-wide maximum (kGridSetWords); the paired launch uses two
 // such sets
 static_assert(kGridSetWords == (2 * kMaxGroups + 1) * kLine, "grid-wide maximum words");
 static_assert(2 * kGridSetWords <= kGridMaxWords, "grid-wide maximum words");
 __device__ __forceinline__ uint32_t* gm_mask(uint32_t* w, int g) { return w + g * kLine; }
 __device__ __forceinline__ uint32_t* gm_max(uint32_t* w, int g) { return w + g * kLine + 1; }
-__device__ __forceinline__ uint32_t* gm_dep(uint32_t* w, int g) { return w + g * kLine + 2; }
-__device__ __forceinline__ uint32_t* gm_flag(uint32_t* w, int g) {
-  return w + (kMaxGroups + g) * kLine;
+__device__ __forceinline__ uint64_t* gm_flag(uint32_t* w, int g) {
+  return reinterpret_cast<uint64_t*>(w + (kMaxGroups + g) * kLine);
 }
 // top line: [0] complete groups, [1] maximum, [2] publish claim, [3] rescue
-// claim, [4] departed groups
+// claim, [4] generation
 __device__ __forceinline__ uint32_t* gm_top(uint32_t* w) { return w + 2 * kMaxGroups * kLine; }
-constexpr int kTopWords = 5;
 // 0, computed from v in a way the compiler cannot see through: an atomic
 // (or address) that takes it waits for v, i.e. for the atomic that produced v.
 __device__ __forceinline__ uint32_t after(uint32_t v) {
@@ -306,37 +308,36 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t atomic_or_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_xchg_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// true if this call claimed the word (0 -> 1)
-__device__ __forceinline__ bool claim_agent(uint32_t* p) {
-  uint32_t expected = 0u;
-  return __hip_atomic_compare_exchange_strong(p, &expected, 1u, __ATOMIC_RELAXED,
+// true if this call moved *p from `from` to from + 1
+__device__ __forceinline__ bool claim_agent(uint32_t* p, uint32_t from) {
+  uint32_t expected = from;
+  return __hip_atomic_compare_exchange_strong(p, &expected, from + 1u, __ATOMIC_RELAXED,
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publish amax (FP32 magnitude bits) to every group's flag, unless another
-// workgroup has claimed that (thread 0).  Returns 0, once every swap it made
-// has returned.
-__device__ __forceinline__ uint32_t gm_publish(uint32_t* w, uint32_t ngroups, uint32_t amax) {
-  if (!claim_agent(gm_top(w) + 2)) return 0u;
-  uint32_t acc = 0u;
-  for (uint32_t i = 0; i < ngroups; ++i) acc |= atomic_xchg_agent(gm_flag(w, (int)i), kPublished | amax);
-  return after(acc);
+// Publish amax (FP32 magnitude bits) for generation gen + 1 to every group's
+// flag, if this call wins the publish claim (thread 0).
+__device__ __forceinline__ bool gm_publish(uint32_t* w, uint32_t ngroups, uint32_t gen,
+                                           uint32_t amax) {
+  if (!claim_agent(gm_top(w) + 2, gen + after(amax))) return false;
+  const uint64_t f = ((uint64_t)(gen + 1u) << 32) | amax;
+  for (uint32_t i = 0; i < ngroups; ++i)
+    __hip_atomic_store(gm_flag(w, (int)i), f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
-// Poll group g's flag up to `limit` times: the amax, or kNoMax (thread 0).
-__device__ __forceinline__ uint32_t gm_wait(uint32_t* w, int g, uint32_t limit) {
+// Poll group g's flag up to `limit` times for generation gen + 1: the amax,
+// or kNoMax (thread 0).
+__device__ __forceinline__ uint32_t gm_wait(uint32_t* w, int g, uint32_t gen, uint32_t limit) {
   for (uint32_t spin = 0; spin < limit; ++spin) {
-    const uint32_t f = load_agent(gm_flag(w, g));
-    if (f & kPublished) return f & ~kPublished;
+    const uint64_t f = __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(f >> 32) == gen + 1u) return (uint32_t)f;
     __builtin_amdgcn_s_sleep(4);
   }
   return kNoMax;
@@ -345,7 +346,8 @@ __device__ __forceinline__ uint32_t gm_wait(uint32_t* w, int g, uint32_t limit) 
 // The largest m over the nblocks workgroups that share the words at w, in
 // every one of them, or kNoMax if the wait ran out (then grid_rescue); block
 // is the calling workgroup's index among them; cfg[0] bounds the polls (0:
-// kSpinLimit).  All threads call it; thread 0 does the work.
+// kSpinLimit).  sh[1] receives the call's generation.  All threads call it;
+// thread 0 does the work.
 __device__ __forceinline__ uint32_t grid_max(uint32_t* w, const uint32_t* cfg, uint32_t m,
                                              uint32_t block, uint32_t nblocks, uint32_t* sh) {
   if (threadIdx.x == 0) {
@@ -353,7 +355,8 @@ __device__ __forceinline__ uint32_t grid_max(uint32_t* w, const uint32_t* cfg, u
     const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
     const uint32_t gsize = min((uint32_t)kGroup, nblocks - (uint32_t)g * kGroup);
     const uint32_t bit = 1u << (block % kGroup);
-    const uint32_t mo = atomic_max_agent(gm_max(w, g), m);
+    const uint32_t gen = load_agent(gm_top(w) + 4);
+    const uint32_t mo = atomic_max_agent(gm_max(w, g), m + after(gen));
     const uint32_t mask = atomic_or_agent(gm_mask(w, g), bit | after(mo)) | bit;
     bool last = false;
     if ((uint32_t)__builtin_popcount(mask) == gsize) {
@@ -364,24 +367,37 @@ __device__ __forceinline__ uint32_t grid_max(uint32_t* w, const uint32_t* cfg, u
     uint32_t res;
     if (last) {
       res = atomic_max_agent(gm_top(w) + 1, 0u);
-      res += gm_publish(w, ngroups, res);
+      const uint32_t z = after((uint32_t)gm_publish(w, ngroups, gen, res));
+      // after the publish claim: close the rescue claim, clear the arrival
+      // words, advance the generation
+      store_agent(gm_top(w) + 3, gen + 1u + z);
+      for (uint32_t i = 0; i < ngroups; ++i) {
+        store_agent(gm_mask(w, (int)i), z);
+        store_agent(gm_max(w, (int)i), z);
+      }
+      store_agent(gm_top(w), z);
+      store_agent(gm_top(w) + 1, z);
+      store_agent(gm_top(w) + 4, gen + 1u + z);
     } else {
       const uint32_t c = *cfg;
-      res = gm_wait(w, g, c != 0 ? c : kSpinLimit);
+      res = gm_wait(w, g, gen, c != 0 ? c : kSpinLimit);
     }
-    *sh = res;
+    sh[0] = res;
+    sh[1] = gen;
   }
   __syncthreads();
-  const uint32_t r = *sh;
+  const uint32_t r = sh[0];
   __syncthreads();
   return r;
 }
 
-// After a wait that ran out (all threads call it): the first such workgroup
-// computes the amax from the group maxima (every arrived workgroup's
-// maximum) and the inputs of the workgroups that have not arrived, which it
-// reads itself, and publishes it; the others wait for that.  share(b, lo, hi)
-// gives workgroup b's range of 16-byte vectors of x; ms is two words of LDS.
+// After a wait that ran out (all threads call it; sh[1] holds the call's
+// generation): the first such workgroup computes the amax from the group
+// maxima (every arrived workgroup's maximum) and the inputs of the
+// workgroups that have not arrived, which it reads itself, and publishes it
+// unless the last arrival did first; the others wait for the flag.
+// share(b, lo, hi) gives workgroup b's range of 16-byte vectors of x; ms is
+// two words of LDS.
 template <class Share>
 __device__ __forceinline__ uint32_t grid_rescue(uint32_t* w, const uint4* x, Share share,
                                                 uint32_t block, uint32_t nblocks, uint32_t* ms,
@@ -389,84 +405,69 @@ __device__ __forceinline__ uint32_t grid_rescue(uint32_t* w, const uint4* x, Sha
   const int t = threadIdx.x;
   const int g = (int)(block / kGroup);
   const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
-  if (t == 0) *sh = claim_agent(gm_top(w) + 3) ? 1u : 0u;
+  const uint32_t gen = sh[1];
   __syncthreads();
-  const bool rescuer = *sh != 0u;
+  if (t == 0) sh[0] = claim_agent(gm_top(w) + 3, gen) ? 1u : 0u;
   __syncthreads();
-  if (!rescuer) {
-    if (t == 0) *sh = gm_wait(w, g, kRescueSpinLimit);
-    __syncthreads();
-    const uint32_t a = *sh;
-    __syncthreads();
-    if (a != kNoMax) return a;
-    // the rescuer has not published (not expected: it is running): reduce
-    // the whole input here, which gives the same value
-    int64_t lo, end;
-    share(nblocks - 1, lo, end);
+  const bool rescuer = sh[0] != 0u;
+  __syncthreads();
+  uint32_t a = kNoMax;
+  if (rescuer) {
+    // group by group: stop if the amax has been published meanwhile (the
+    // missing workgroups have arrived), else read the inputs of the group's
+    // workgroups that have not arrived yet; a bit read as set was set after
+    // that workgroup's maximum was in its group's word, which is read last
     uint32_t m = 0;
-    for (int64_t i = t; i < end; i += kThreads) m = max(m, absmax8(x[i]) << 16);
-    return block_max_u32<kThreads>(m, red);
+    bool done = false;
+    for (uint32_t i = 0; i < ngroups && !done; ++i) {
+      if (t == 0) {
+        const uint32_t gsize = min((uint32_t)kGroup, nblocks - i * kGroup);
+        const uint32_t all = gsize == 32u ? 0xFFFFFFFFu : (1u << gsize) - 1u;
+        const uint64_t f =
+            __hip_atomic_load(gm_flag(w, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ms[0] = (uint32_t)(f >> 32) == gen + 1u ? (uint32_t)f : kNoMax;
+        ms[1] = ~load_agent(gm_mask(w, (int)i)) & all;
+      }
+      __syncthreads();
+      const uint32_t f = ms[0];
+      uint32_t bits = ms[1];
+      __syncthreads();
+      if (f != kNoMax) {
+        a = f;
+        done = true;
+      } else {
+        while (bits) {
+          const uint32_t b = i * kGroup + (uint32_t)(__builtin_ffs((int)bits) - 1);
+          bits &= bits - 1u;
+          int64_t lo, hi;
+          share(b, lo, hi);
+          for (int64_t k = lo + t; k < hi; k += kThreads) m = max(m, absmax8(x[k]) << 16);
+        }
+      }
+    }
+    if (!done) {
+      if ((uint32_t)t < ngroups) m = max(m, load_agent(gm_max(w, t)));
+      m = block_max_u32<kThreads>(m, red);
+      // a lost claim means the last arrival published first: take its amax
+      if (t == 0) sh[0] = gm_publish(w, ngroups, gen, m) ? m : gm_wait(w, g, gen, kRescueSpinLimit);
+      __syncthreads();
+      a = sh[0];
+      __syncthreads();
+    }
+  } else {
+    if (t == 0) sh[0] = gm_wait(w, g, gen, kRescueSpinLimit);
+    __syncthreads();
+    a = sh[0];
+    __syncthreads();
   }
-  // group by group: stop if the amax has been published meanwhile (the
-  // missing workgroups have arrived), else read the inputs of the group's
-  // workgroups that have not arrived yet; a bit read as set was set after
-  // that workgroup's maximum was in its group's word, which is read last
+  if (a != kNoMax) return a;
+  // the flag did not come (not expected: the rescuer or the last arrival is
+  // running): reduce the whole input here, which gives the same value
+  int64_t lo, end;
+  share(nblocks - 1, lo, end);
   uint32_t m = 0;
-  for (uint32_t i = 0; i < ngroups; ++i) {
-    if (t == 0) {
-      const uint32_t gsize = min((uint32_t)kGroup, nblocks - i * kGroup);
-      const uint32_t all = gsize == 32u ? 0xFFFFFFFFu : (1u << gsize) - 1u;
-      ms[0] = load_agent(gm_flag(w, g));
-      ms[1] = ~load_agent(gm_mask(w, (int)i)) & all;
-    }
-    __syncthreads();
-    const uint32_t f = ms[0];
-    uint32_t bits = ms[1];
-    __syncthreads();
-    if (f & kPublished) return f & ~kPublished;
-    while (bits) {
-      const uint32_t b = i * kGroup + (uint32_t)(__builtin_ffs((int)bits) - 1);
-      bits &= bits - 1u;
-      int64_t lo, hi;
-      share(b, lo, hi);
-      for (int64_t k = lo + t; k < hi; k += kThreads) m = max(m, absmax8(x[k]) << 16);
-    }
-  }
-  if ((uint32_t)t < ngroups) m = max(m, load_agent(gm_max(w, t)));
-  m = block_max_u32<kThreads>(m, red);
-  // the last arrival may have published first: the same value
-  if (t == 0) *sh = m + gm_publish(w, ngroups, m);
-  __syncthreads();
-  const uint32_t a = *sh;
-  __syncthreads();
-  return a;
-}
-
-// Count the calling workgroup out; the last one clears every word for the
-// next call.  All threads call it, after the workgroup's last use of the
-// words.
-__device__ __forceinline__ void grid_depart(uint32_t* w, uint32_t block, uint32_t nblocks,
-                                            uint32_t* sh) {
-  const int t = threadIdx.x;
-  const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
-  if (t == 0) {
-    const int g = (int)(block / kGroup);
-    const uint32_t gsize = min((uint32_t)kGroup, nblocks - (uint32_t)g * kGroup);
-    const uint32_t d = atomic_add_agent(gm_dep(w, g), 1u);
-    bool last = false;
-    if (d + 1 == gsize) last = atomic_add_agent(gm_top(w) + 4, 1u + after(d)) + 1 == ngroups;
-    *sh = last ? 1u : 0u;
-  }
-  __syncthreads();
-  if (*sh != 0u) {
-    for (uint32_t i = t; i < ngroups; i += kThreads) {
-      store_agent(gm_mask(w, (int)i), 0u);
-      store_agent(gm_max(w, (int)i), 0u);
-      store_agent(gm_dep(w, (int)i), 0u);
-      store_agent(gm_flag(w, (int)i), 0u);
-    }
-    if (t < kTopWords) store_agent(gm_top(w) + t, 0u);
-  }
+  for (int64_t i = t; i < end; i += kThreads) m = max(m, absmax8(x[i]) << 16);
+  return block_max_u32<kThreads>(m, red);
 }
 
 // One tensor of the paired current-scaling launch.
@@ -561,7 +562,6 @@ __device__ __forceinline__ void amax_cast_held(const PairTensor& T, uint32_t b,
 #pragma unroll
     for (int l = 0; l < L; ++l) store(lv[l][t], U + l);
   }
-  grid_depart(T.gw, b, T.nblocks, sh);
 }
 
 // Current scaling of two tensors (a GEMM's two operands) in one launch:
@@ -572,13 +572,13 @@ template <int FA, int FB, int U, int L>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 k_amax_cast_pair(PairArgs a) {
   __shared__ uint32_t red[kThreads / 64];
-  __shared__ uint32_t sh;
+  __shared__ uint32_t sh[2];
   __shared__ uint32_t ms[2];
   __shared__ __attribute__((aligned(16))) uint4 lv[L][kThreads];
   if (blockIdx.x < a.t[0].nblocks)
-    amax_cast_held<FA, U, L>(a.t[0], blockIdx.x, lv, red, &sh, ms);
+    amax_cast_held<FA, U, L>(a.t[0], blockIdx.x, lv, red, sh, ms);
   else
-    amax_cast_held<FB, U, L>(a.t[1], blockIdx.x - a.t[0].nblocks, lv, red, &sh, ms);
+    amax_cast_held<FB, U, L>(a.t[1], blockIdx.x - a.t[0].nblocks, lv, red, sh, ms);
 }
 
 // Current scaling in one launch of one tensor: the body above with every
@@ -590,10 +590,10 @@ __attribute__((amdgpu_waves_per_eu(U >= 24 ? 4 : 1, 8))) void k_amax_cast(
     const uint32_t* __restrict__ cfg, float* __restrict__ amax,
     float* __restrict__ scale, float* __restrict__ scale_inv) {
   __shared__ uint32_t red[kThreads / 64];
-  __shared__ uint32_t sh;
+  __shared__ uint32_t sh[2];
   __shared__ uint32_t ms[2];
   const PairTensor T{x, nvec, q, gw, cfg, amax, scale, scale_inv, gridDim.x};
-  amax_cast_held<FMT, U, 0>(T, blockIdx.x, nullptr, red, &sh, ms);
+  amax_cast_held<FMT, U, 0>(T, blockIdx.x, nullptr, red, sh, ms);
 }
 
 // 4x4 byte transpose of rows a,b,c,d (one 32-bit word each, byte i = column i)
