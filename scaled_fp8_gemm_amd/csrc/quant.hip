@@ -1012,6 +1012,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_t(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) uint4 cmax[2][4][16];
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][128 * 32];
   __shared__ uint32_t colb[KIND == kTMX ? 2 : 1][128];   // MX: a column's 4 E8M0 bytes
+  __shared__ uint32_t rowb[KIND == kTMX ? 2 : 1][128];   // MX: a row's 4 E8M0 bytes
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int tc = t & 15, tr = t >> 4, qd = lane >> 4;   // qd: the lane's 16-lane row
   const int64_t row_blocks = cols / RB, col_blocks = rows / RB;
@@ -1116,10 +1117,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_t(const uint16_t* __restrict
         sr[5] = __uint_as_float(dpp<0xAA>(__float_as_uint(s1)));
         sr[6] = __uint_as_float(dpp<0xFF>(__float_as_uint(s0)));
         sr[7] = __uint_as_float(dpp<0xFF>(__float_as_uint(s1)));
-        if (q != nullptr && valid) {
-          uint8_t* o = static_cast<uint8_t*>(sq) + (row + 2 * b) * row_blocks + col / 32;
-          o[0] = (uint8_t)by0;
-          o[row_blocks] = (uint8_t)by1;
+        // byte k of rowb[r] is tile row r's scale for column block k; written
+        // out after the tile's barrier, one dword per row
+        if (valid) {
+          uint8_t* rb = reinterpret_cast<uint8_t*>(rowb[buf]) + (8 * tr + 2 * b) * 4 + (tc >> 2);
+          rb[0] = (uint8_t)by0;
+          rb[4] = (uint8_t)by1;
         }
         // MX columns: lanes of 16-lane row qd compute columns 2qd, 2qd+1
         const uint32_t pc = pick4(C[0], C[1], C[2], C[3], qd);
@@ -1164,6 +1167,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_t(const uint16_t* __restrict
           *reinterpret_cast<uint32_t*>(o) = b4;
         } else {
           for (int ww = 0; ww < rv / 32; ++ww) o[ww] = (uint8_t)(b4 >> (8 * ww));
+        }
+      }
+      // row scales likewise: thread 128 + r < 128 + rv writes row r's bytes
+      // for the tile's cv / 32 column blocks
+      if (q != nullptr && t >= 128 && t - 128 < rv) {
+        const int r = t - 128;
+        const uint32_t b4 = rowb[buf][r];
+        uint8_t* o = static_cast<uint8_t*>(sq) + (r0 + r) * row_blocks + c0 / 32;
+        if (cv == 128 && (row_blocks & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(o) = b4;
+        } else {
+          for (int k = 0; k < cv / 32; ++k) o[k] = (uint8_t)(b4 >> (8 * k));
         }
       }
     }
