@@ -15,9 +15,11 @@ int device_cu_count();
 //                                   per output tile for the GEMM's fused amax
 //   [kGridWordsAt, +kGridMaxWords)  grid-wide maxima of the one-launch current
 //                                   scaling (two sets, one per tensor of the
-//                                   paired launch; counters, maxima and flags,
+//                                   paired launch; arrival masks, maxima,
+//                                   flags, claims and the call's generation,
 //                                   one 128-byte line each); zero before first
-//                                   use, and left zero by every launch
+//                                   use, and left ready for the next call by
+//                                   every launch
 //   [kConfigAt, +kConfigWords)      word 0: bound on the polls of the
 //                                   grid-wide wait (0 = the default)
 constexpr int kWorkspaceWords = 1 << 16;
@@ -32,7 +34,7 @@ constexpr int kWorkspaceTotalWords = kConfigAt + kConfigWords;
 constexpr int kMaxPartials = 2048;
 constexpr int kGridSetWords = (2 * (kMaxPartials / 32) + 1) * 32;
 // Where one current-scaling call reduces: kMaxPartials partial maxima, one
-// set of grid-wide maximum words (zero before first use, left zero), and
+// set of grid-wide maximum words (zero before first use, left ready), and
 // the config word (the wait bound, 0 = default).
 struct CurrentWs {
   uint32_t* part;
