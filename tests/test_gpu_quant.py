@@ -537,3 +537,55 @@ def test_current_scaling_wait_bound_fallback(F, orc, calls, spike):
     torch.cuda.synchronize()
     for j in range(2):
         assert np.array_equal(bytes8(ref[j][0]), bytes8(outs[j][0]))
+
+
+# Workspace words of the one-launch grid-wide maximum (an internal layout,
+# forged here to reach a state that 2^32 - 2 earlier calls would leave):
+# set s starts at word 65536 + 4128 s; its top line at +4096 holds the
+# publish claim [2], the rescue claim [3] and the generation [4]; group g's
+# flag is the 64-bit word at +(64 + g) * 32 (low half amax, high half the
+# generation that published it).
+_GRID_AT, _SET_WORDS, _TOP_AT, _FLAG_AT = 65536, 4128, 4096, 64 * 32
+
+
+def _forge_generation(ws, gen):
+    words = ws.view(torch.int32)
+    g = torch.tensor(np.array([gen], np.uint32).view(np.int32), device=DEV)
+    for s in range(2):
+        base = _GRID_AT + s * _SET_WORDS
+        words[base + _TOP_AT + 2: base + _TOP_AT + 5] = g
+        for grp in range(64):
+            words[base + _FLAG_AT + grp * 32 + 1] = g    # published by generation G itself
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wait_polls", [0, 1])
+@pytest.mark.parametrize("calls", ["one", "pair"])
+def test_current_scaling_generation_wraps(F, orc, calls, wait_polls):
+    """The grid-wide maximum tags flags and claims with a 32-bit generation
+    that every call advances by one; calls across its wrap (0xFFFFFFFE ->
+    0xFFFFFFFF -> 0 -> 1) give the oracle's bytes, with the default wait
+    bound and with a one-poll bound (the rescue path), on one workspace."""
+    shapes = ((4096, 4096), (11008, 4096))
+    xs = [rand_bits(sh, 970 + j, 2.0 if j == 0 else 0.02) for j, sh in enumerate(shapes)]
+    dx = [dev_bf16(x) for x in xs]
+    ws = F.workspace(wait_polls=wait_polls)
+    torch.cuda.synchronize()
+    _forge_generation(ws, 0xFFFFFFFE)
+    for rep in range(4):
+        outs = [_current_outputs(sh) for sh in shapes]
+        if calls == "pair":
+            F.fp8_quantize_pair_current(dx[0], E4M3, *outs[0], dx[1], E4M3, *outs[1],
+                                        workspace=ws)
+        else:
+            for d, o in zip(dx, outs):
+                F.fp8_quantize_tensor_current(d, E4M3, o[0], None, *o[1:], workspace=ws)
+        torch.cuda.synchronize()
+        for j in range(2):
+            _check_current(orc, xs[j], E4M3, *outs[j], label=f"{calls} wrap rep {rep} tensor {j}")
+    # every call took the one-launch path and advanced its set's generation
+    # past the wrap: 4 pair calls (one per set), or 8 single calls on set 0
+    words = ws.view(torch.int32).cpu().numpy().view(np.uint32)
+    want = {0: 2, 1: 2} if calls == "pair" else {0: 6}
+    for s, g in want.items():
+        assert words[_GRID_AT + s * _SET_WORDS + _TOP_AT + 4] == g, (calls, s)
