@@ -3,8 +3,12 @@
 // order NULL -> enum -> shape -> alignment (a NULL data pointer is accepted
 // for an empty tensor, so the NULL check of data follows the shape check),
 // and only then enqueues kernels on the caller's stream.  Nothing here or
-// in the launchers allocates, synchronises or keeps state between calls:
-// the amax-producing calls reduce through the caller's workspace.
+// in the launchers allocates or synchronises, and the only state kept
+// between calls is read-only device facts cached per device (CU count,
+// occupancy-derived grid sizes): the amax-producing calls reduce through
+// the caller's workspace.  The one exception is
+// fp8_quantize_tensor_current_noalloc, which reduces through a static device
+// array and keeps its address per device.
 #include "fp8sg.h"
 
 #include <stdint.h>
