@@ -106,10 +106,12 @@ typedef struct {
  * use: zero-fills it with a kernel on `stream` (no memset, so the call may be
  * captured in a graph) and sets the bound on the grid-wide wait of the
  * one-launch current scaling.
- *   wait_polls  0: the default bound (2^15 polls, several milliseconds);
- *               n > 0: n polls.  A workgroup whose wait runs out reduces the
- *               whole input itself, so results never change, only speed;
- *               1 makes that slow path the common one (for tests).
+ *   wait_polls  0: the default bound (2^12 polls, about a millisecond);
+ *               n > 0: n polls.  When a workgroup's wait runs out, one
+ *               workgroup completes the amax from the maxima already in and
+ *               the inputs of the workgroups that have not arrived, and
+ *               publishes it, so results never change, only speed; 1 makes
+ *               that path the common one (for tests).
  * Errors: NULL workspace; wait_polls < 0 (FP8_ERR_SHAPE); alignment. */
 fp8_status_t fp8_workspace_init(void* workspace, int32_t wait_polls, void* stream);
 
@@ -154,8 +156,9 @@ fp8_status_t fp8_quantize_tensor(const void* x_bf16, int64_t rows, int64_t cols,
  * Otherwise two launches: the amax pass, then the cast, whose workgroups
  * each reduce the amax pass's partial maxima and derive the scale
  * themselves.  The one-launch grid waits on itself: if other work keeps
- * part of it from being resident for several milliseconds, the waiting
- * workgroups reduce all of x themselves (same result, slower).
+ * part of it from being resident for about a millisecond, one waiting
+ * workgroup reads the shares of the missing workgroups itself and publishes
+ * the amax (same result, slower).
  *   x_bf16     [rows][cols] BF16, cols % 16 == 0
  *   q          out uint8 [rows][cols];  qT  out [cols][rows], nullable
  *              (rows % 16 == 0)

@@ -188,8 +188,9 @@ def test_quantize_tensor_current_concurrent_streams(F, orc):
     """Two one-launch current-scaling calls running at once on different
     streams, each grid as large as the device holds.  However the two grids'
     workgroups interleave (one grid can keep the other from being resident),
-    both results are the oracle's, bit for bit: a workgroup whose grid-wide
-    wait runs out reduces the whole input itself."""
+    both results are the oracle's, bit for bit: when a grid-wide wait runs
+    out, one workgroup completes the amax from the maxima already in and the
+    inputs of the workgroups that have not arrived."""
     shape = (4096, 8192)
     xs = [rand_bits(shape, 700 + i, 3.0) for i in range(2)]
     dx = [dev_bf16(x) for x in xs]
