@@ -46,8 +46,10 @@ def run_gemm(F, which, A, B, fa, fb, sca, scb, sa, sb, M, N, K):
     return bits16(out)
 
 
+# K <= 4096 spreads the next step's loads over four fragment columns; K =
+# 4224 (33 steps) takes the other schedule, with ragged row and column tiles
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (600, 520, 400), (17, 33, 16), (1, 1, 128),
-                                   (513, 257, 1024), (300, 700, 2048)])
+                                   (513, 257, 1024), (300, 700, 2048), (300, 520, 4224)])
 @pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
 def test_tensor_scaled(F, orc, M, N, K, fa, fb):
     A = rand_codes((M, K), fa, M + K)
