@@ -590,3 +590,33 @@ def test_current_scaling_generation_wraps(F, orc, calls, wait_polls):
     want = {0: 2, 1: 2} if calls == "pair" else {0: 6}
     for s, g in want.items():
         assert words[_GRID_AT + s * _SET_WORDS + _TOP_AT + 4] == g, (calls, s)
+
+
+@pytest.mark.parametrize("wait_polls", [0, 1])
+def test_current_scaling_calls_of_many_sizes_share_a_workspace(F, orc, wait_polls):
+    """Single and paired one-launch calls of different sizes (so different
+    numbers of workgroup groups), and a transposed-copy call that takes the
+    two-launch path, all in a row on one workspace: every call matches the
+    oracle bit for bit (the grid-wide words one call leaves are valid for
+    any next call, whatever its grid)."""
+    ws = F.workspace(wait_polls=wait_polls)
+    seq = [("one", (4096, 4096)), ("one", (256, 256)), ("pair", ((11008, 4096), (64, 64))),
+           ("one", (2056, 8208)), ("t", (512, 768)), ("pair", ((256, 256), (4096, 4096))),
+           ("one", (16, 16)), ("one", (11008, 4096))]
+    for i, (kind, shp) in enumerate(seq):
+        shapes = shp if kind == "pair" else (shp,)
+        xs = [rand_bits(sh, 1100 + 10 * i + j, 1.5 if j == 0 else 0.03) for j, sh in enumerate(shapes)]
+        dx = [dev_bf16(x) for x in xs]
+        outs = [_current_outputs(sh) for sh in shapes]
+        if kind == "pair":
+            F.fp8_quantize_pair_current(dx[0], E4M3, *outs[0], dx[1], E4M3, *outs[1], workspace=ws)
+        elif kind == "t":
+            qT = empty_dev(shp[::-1], torch.uint8)
+            F.fp8_quantize_tensor_current(dx[0], E4M3, outs[0][0], qT, *outs[0][1:], workspace=ws)
+        else:
+            F.fp8_quantize_tensor_current(dx[0], E4M3, outs[0][0], None, *outs[0][1:], workspace=ws)
+        torch.cuda.synchronize()
+        for j in range(len(shapes)):
+            _check_current(orc, xs[j], E4M3, *outs[j], label=f"call {i} {kind} {shapes[j]}")
+        if kind == "t":
+            assert np.array_equal(bytes8(qT), bytes8(outs[0][0]).T), f"call {i} qT"
