@@ -175,7 +175,7 @@ fp8_status_t fp8_quantize_tensor_current(const void* x_bf16, int64_t rows, int64
  * memory (code under graph capture, tight serving loops, harnesses that
  * forbid allocation): the same results, but no workspace argument.  The
  * call reduces through a static scratch array of the library, 24832 bytes
- * per GPU (2048 partial maxima, 65 lines of grid-wide maximum words, one
+ * per GPU (2048 partial maxima, 129 lines of grid-wide maximum words, one
  * settings line), held from the first call on a GPU until the process ends;
  * that first call takes the array's device address and clears it with a
  * kernel on `stream`.  The scratch suffices for every tensor the regular
